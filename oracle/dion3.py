@@ -310,12 +310,13 @@ def apply_rows(W, M, idx, O, eta: float, wd: float, mu: float, fmt: str):
         M[idx] = mu * M[idx]
         return W, M
     eta32, mu32 = f32(eta), f32(mu)
+    A = W
     if wd != 0.0:
         u = f32(1.0 - eta32 * f32(wd))
-        W = round_to(round_to(u * W, "f32"), fmt)
-    Ws = W[idx]
-    upd = round_sum(Ws, -eta32 * np.asarray(O, dtype=np.float64), "f32")
-    W[idx] = round_to(upd, fmt)
+        A = round_to(u * W, "f32")          # fp32 value of the decayed weights
+    upd = round_sum(A[idx], -eta32 * np.asarray(O, dtype=np.float64), "f32")
+    W = round_to(A, fmt)                    # unselected lines: one cast of u*w
+    W[idx] = round_to(upd, fmt)             # selected lines: one cast of u*w - eta*o
     M[idx] = round_to(mu32 * M[idx], fmt)
     return W, M
 

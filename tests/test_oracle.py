@@ -345,19 +345,28 @@ def test_zero_selected_submatrix_leaves_w():
     assert list(out["idx"]) == [0, 1]
 
 
-def test_apply_rows_fused_rounding_exact():
-    """w' = bf16(fp32(w - eta o)) with a single fp32 rounding: exact rationals."""
+@pytest.mark.parametrize("wd", [0.0, 0.1])
+def test_apply_rows_fused_rounding_exact(wd):
+    """Selected lines: w' = bf16(fp32(a - eta o)) with a = fp32(u w) (a = w when
+    wd = 0), i.e. fp32 arithmetic and ONE cast back; unselected lines: bf16(a).
+    Checked with exact rationals."""
     rng = np.random.default_rng(8)
     W = O.round_to(rng.standard_normal((6, 50)) * 0.02, "bf16")
     M = O.round_to(rng.standard_normal((6, 50)), "bf16")
     Ov = O.round_to(rng.standard_normal((3, 50)) * 0.05, "f16")
     idx = np.array([0, 2, 5])
     eta = O.f32(0.04)
-    W2, _ = O.apply_rows(W, M, idx, Ov, 0.04, 0.0, 0.95, "bf16")
-    for r, i in enumerate(idx):
+    u = Fraction(_exact_round(1 - Fraction(eta) * Fraction(O.f32(wd)), "f32"))
+    W2, _ = O.apply_rows(W, M, idx, Ov, 0.04, wd, 0.95, "bf16")
+    sel = {int(i): r for r, i in enumerate(idx)}
+    for i in range(6):
         for j in range(50):
-            t = _exact_round(Fraction(float(W[i, j])) - Fraction(eta) * Fraction(float(Ov[r, j])), "f32")
-            assert W2[i, j] == _exact_round(Fraction(t), "bf16")
+            a = Fraction(float(W[i, j])) if wd == 0 else Fraction(_exact_round(u * Fraction(float(W[i, j])), "f32"))
+            if i in sel:
+                t = _exact_round(a - Fraction(eta) * Fraction(float(Ov[sel[i], j])), "f32")
+            else:
+                t = float(a)
+            assert W2[i, j] == _exact_round(Fraction(t), "bf16"), (i, j)
 
 
 def test_fp16_storage_model_within_tolerance():
