@@ -1,0 +1,209 @@
+/*
+ * dion3.h -- C ABI of the MI355X (gfx950) Dion3 optimizer-step hot path.
+ *
+ * The method is the one described in "Dion3: Full-Stack Orthogonal Updates"
+ * (paper text; section numbers inferred from its cross-references):
+ *   momentum   M <- M + G                                  (Section 6)
+ *   selection  the k = ceil(f n) rows of largest l1 norm   (Section 6)
+ *   Gram Newton-Schulz of M[S,:], restart after iter 2     (Section 4)
+ *   update     W[S,:] <- W[S,:] - eta O, one rounding;     (Section 6)
+ *              M[S,:] <- mu M[S,:]  (error feedback)
+ *
+ * Conventions shared by every entry point:
+ *   - Matrices are row-major; a "group" is `batch` matrices of one shape laid
+ *     out `batch_stride` elements apart.
+ *   - Canonical orientation: the selection axis has length n and the other
+ *     axis length m.  sel_axis 0 selects rows (n = rows, m = cols), 1 selects
+ *     columns (n = cols, m = rows); -1 picks the smaller dimension, rows on a
+ *     tie (Section 6: select along the smaller dimension when not sharded).
+ *   - All tensor pointers are device pointers owned by the caller; the
+ *     library never allocates, frees or retains them.  Scalars and parameter
+ *     structs are host values read during the call.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call is
+ *     asynchronous and stream-ordered, does no host synchronisation and no
+ *     allocation, and is deterministic run to run.
+ *   - Return value: DION3_OK (0) or a negative status.  Arguments are
+ *     validated before anything is launched; on an error nothing is written.
+ *     DION3_ERR_HIP means a launch failed (hipGetLastError was not success).
+ *   - A workspace must not be used by two calls that may run concurrently.
+ */
+#ifndef DION3_H
+#define DION3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { DION3_F32 = 0, DION3_F16 = 1, DION3_BF16 = 2 } dion3_dtype;
+
+enum {
+  DION3_OK = 0,
+  DION3_ERR_INVALID_ARG = -1,   /* null pointer, size <= 0, k outside [1, n], bad dtype */
+  DION3_ERR_UNSUPPORTED = -2,   /* valid but not implemented (e.g. n > 32768 in top-k) */
+  DION3_ERR_WORKSPACE = -3,     /* workspace missing or smaller than required */
+  DION3_ERR_HIP = -4            /* a HIP launch or runtime call failed */
+};
+
+/* A batch of same-shape matrices (W, G and M share this description). */
+typedef struct {
+  int rows, cols;              /* stored shape of each matrix, leading dimension = cols */
+  int batch;                   /* number of matrices */
+  long long batch_stride;      /* elements between consecutive matrices, >= rows*cols */
+  int dtype;                   /* dion3_dtype of W, G and M: DION3_F32 or DION3_BF16 */
+  int sel_axis;                /* -1 auto, 0 rows, 1 columns */
+} dion3_group;
+
+/* Newton-Schulz parameters (Section 2 polynomial p_t(x) = a_t x + b_t x^3 + c_t x^5;
+ * Section 4 restart).  coeffs is a host array [T][3] of (a_t, b_t, c_t).
+ * Bit t of restart_mask (1 <= t < T) restarts after iteration t; the pages'
+ * setting is T = 5, restart_mask = 1u << 2.  eps guards X / (||X||_F + eps).
+ * ns_dtype is the storage type of every Newton-Schulz intermediate:
+ * DION3_F16 (the pages' half-precision choice) or DION3_F32. */
+typedef struct {
+  int T;
+  const double* coeffs;
+  unsigned restart_mask;
+  float eps;
+  int ns_dtype;
+} dion3_ns_params;
+
+/* ---------------------------------------------------------------- helpers */
+
+/* k = ceil(f * n) for the exact product of the given double f and n, clamped
+ * to [1, n] (Section 6).  Returns k, or DION3_ERR_INVALID_ARG unless n >= 1
+ * and 0 < f <= 1. */
+int dion3_k_from_fraction(int n, double f);
+
+/* Canonical sizes of a group: *n = length of the selection axis, *m = the
+ * other axis, *axis = 0 (rows) or 1 (columns).  Any output pointer may be NULL. */
+int dion3_canonical(const dion3_group* g, int* n, int* m, int* axis);
+
+/* Human-readable name of a status code (static storage). */
+const char* dion3_status_string(int status);
+
+/* ------------------------------------------------ momentum and selection */
+
+/* Workspace bytes dion3_momentum_rowsel needs for this group (>= 256). */
+size_t dion3_rowsel_workspace_bytes(const dion3_group* g);
+
+/* Momentum accumulation fused with the selection keys, then top-k (Section 6).
+ *   M      [batch][rows][cols], updated in place: M <- round(M + G), where the
+ *          sum is formed in fp32 and rounded once to the storage type.
+ *   G      [batch][rows][cols], read only.
+ *   idx    out [batch][k] int32: per matrix the k canonical lines with the
+ *          largest l1 norm (ties to the lower index, a NaN norm counts as
+ *          +infinity), listed in ascending order.
+ *   keys   out [batch][n] fp64 l1 norms of the canonical lines (may be NULL).
+ *   sel_sqnorm out [batch] fp64: sum of squares of the selected lines of M,
+ *          i.e. ||M[S,:]||_F^2 (may be NULL).
+ * Norms are accumulated in fp64 in a fixed order.  Requires n <= 32768. */
+int dion3_momentum_rowsel(const dion3_group* g, void* M, const void* G, int k,
+                          int32_t* idx, double* keys, double* sel_sqnorm,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------- gather + scale */
+
+/* X[b] = M[b][S_b, :] / (sqrt(sel_sqnorm[b]) + eps) in canonical orientation
+ * (Section 2: Frobenius normalisation of the Newton-Schulz input).
+ *   X      out [batch][k][m] in x_dtype (DION3_F16 or DION3_F32), packed.
+ *   sel_sqnorm  [batch] fp64 as produced by dion3_momentum_rowsel. */
+int dion3_gather_rows(const dion3_group* g, const void* M, const int32_t* idx, int k,
+                      const double* sel_sqnorm, float eps, int x_dtype, void* X,
+                      void* stream);
+
+/* -------------------------------------------------- Gram Newton-Schulz */
+
+/* Workspace bytes dion3_gram_ns needs. */
+size_t dion3_gram_ns_workspace_bytes(int batch, int k, int m, int ns_dtype);
+
+/* Gram Newton-Schulz with restarts (Section 4) on already normalised inputs.
+ *   X0  [batch][k][m] in p->ns_dtype, k <= m, read only.
+ *   O   out [batch][k][m] in p->ns_dtype: the Newton-Schulz output.
+ * Per pass on R = X X^T:  Z = a I + b R + c R^2;  Q = Z (first iteration) or
+ * Q Z;  R = Z R Z (except on the last iteration); the pass ends X <- Q X.
+ * Symmetric products compute the lower triangle and mirror it. */
+int dion3_gram_ns(int batch, int k, int m, const dion3_ns_params* p, const void* X0,
+                  void* O, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------- symmetric building blocks
+ * (Section 5: triangular tile schedule, mirrored write-back, diagonal tiles
+ * written once.)  dtype: DION3_F16, DION3_BF16 or DION3_F32 for operands and
+ * result; accumulation is fp32.  Matrices are packed (leading dim = cols). */
+
+/* C = alpha A A^T + beta C, A [batch][n][kdim], C [batch][n][n] symmetric.
+ * With beta == 0, C is not read. */
+int dion3_syrk(int batch, int n, int kdim, int dtype, const void* A, long long strideA,
+               void* C, long long strideC, float alpha, float beta, void* stream);
+
+/* C = alpha A A + beta B + gamma I for symmetric A, B [batch][n][n]. */
+int dion3_sym_sq_add(int batch, int n, int dtype, const void* A, long long strideA,
+                     const void* B, long long strideB, void* C, long long strideC,
+                     float alpha, float beta, float gamma, void* stream);
+
+/* C = alpha A B for symmetric A, B whose product is symmetric (commuting
+ * polynomials of one Gram matrix); the lower triangle is computed and mirrored. */
+int dion3_sym_mul(int batch, int n, int dtype, const void* A, long long strideA,
+                  const void* B, long long strideB, void* C, long long strideC,
+                  float alpha, void* stream);
+
+/* Y = alpha Q X for symmetric Q [batch][k][k] and X [batch][k][m] (the
+ * rectangular multiply closing a Gram Newton-Schulz pass).  in_dtype is the
+ * dtype of Q and X, out_dtype that of Y (DION3_F16 or DION3_F32 with f16 in,
+ * same as input otherwise). */
+int dion3_gemm(int batch, int k, int m, int in_dtype, const void* Q, long long strideQ,
+               const void* X, long long strideX, int out_dtype, void* Y, long long strideY,
+               float alpha, void* stream);
+
+/* ------------------------------------------------------------ the update */
+
+/* Fused-rounding update and error feedback (Section 6).  With
+ * u = fp32(1 - eta*wd):
+ *   every line of W (only if wd != 0):  a = fp32(u * w)
+ *   selected lines:   W <- round(fp32(a - eta * O))   (one fp32 rounding, one cast)
+ *                     M <- round(mu * M)              (exact product, one rounding)
+ *   other lines:      W <- round(a) if wd != 0, M untouched.
+ *   O   [batch] slices of [k][m] (o_stride elements apart), canonical
+ *       orientation, o_dtype DION3_F16 or DION3_F32.  eta, wd, mu are fp32. */
+int dion3_apply_rows(const dion3_group* g, void* W, void* M, const int32_t* idx, int k,
+                     const void* O, int o_dtype, long long o_stride,
+                     float eta, float wd, float mu, void* stream);
+
+/* ------------------------------------------------------------ whole step */
+
+/* Workspace bytes dion3_step needs for these groups (k[i] per group). */
+size_t dion3_step_workspace_bytes(int n_groups, const dion3_group* groups, const int* k,
+                                  const dion3_ns_params* p);
+
+/* One optimizer step over several groups (Muon flavour of the update rule,
+ * Section 6, with Gram Newton-Schulz, Section 4).  For every group i:
+ * dion3_momentum_rowsel, dion3_gather_rows; groups whose canonical (k, m)
+ * agree are then orthogonalised in one batched dion3_gram_ns call (the pages'
+ * megabatching of same-shape matrices, on one GPU); finally
+ * dion3_apply_rows.  W[i], M[i], G[i] are the group tensors, idx[i] receives
+ * the [batch][k[i]] selected indices.  eta, wd, mu as in dion3_apply_rows
+ * (one value for all groups).  Everything is enqueued on `stream`. */
+int dion3_step(int n_groups, const dion3_group* groups, void* const* W, void* const* M,
+               const void* const* G, const int* k, int32_t* const* idx,
+               const dion3_ns_params* p, float eta, float wd, float mu,
+               void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------ measurement */
+
+/* Per-kernel timing with hipEvents, for benchmarks.  dion3_timing_enable(n)
+ * creates a pool of n event pairs (n = 0 disables and frees it); while enabled
+ * every launch of the library records an event pair on its stream.  This is
+ * the only call that allocates.  dion3_timing_report writes one line per
+ * kernel name, "name count total_ms\n", into buf (synchronising on the
+ * recorded events) and clears the pool.  Returns the bytes written or a
+ * negative status. */
+int dion3_timing_enable(int max_launches);
+int dion3_timing_report(char* buf, size_t buf_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DION3_H */

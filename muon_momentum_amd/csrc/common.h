@@ -1,0 +1,127 @@
+// Internal helpers shared by the HIP sources of libdion3 (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dion3.h"
+
+namespace dion3 {
+
+typedef _Float16 f16;
+typedef uint16_t bf16_t;   // raw bfloat16 bits
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bfx8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- rounding
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+// fp64 -> bf16 with a single round-to-nearest-even of the fp64 value.
+__device__ __forceinline__ bf16_t f64_to_bf16(double d) {
+  uint64_t u = (uint64_t)__double_as_longlong(d);
+  const uint32_t E = (uint32_t)((u >> 52) & 0x7ff);
+  if (E == 0x7ff) {                                 // inf or NaN
+    if (u & 0x000fffffffffffffull) return (bf16_t)(0x7fc0u | ((u >> 48) & 0x8000u));
+    return (bf16_t)(0x7f80u | ((u >> 48) & 0x8000u));
+  }
+  if (E >= 897) {                                   // |d| >= 2^-126: bf16 normal range
+    u += (1ull << 44) - 1ull + ((u >> 45) & 1ull);  // round the significand to 8 bits
+    u &= ~((1ull << 45) - 1ull);
+    const float f = (float)__longlong_as_double((long long)u);   // exact (or inf)
+    return (bf16_t)(__float_as_uint(f) >> 16);
+  }
+  // bf16 subnormal range: quantum 2^-133
+  const double q = rint(d * 0x1p133) * 0x1p-133;     // exact scaling, RNE
+  return (bf16_t)(__float_as_uint((float)q) >> 16);
+}
+
+template <typename T> struct Store;
+template <> struct Store<float> {
+  __device__ static float to_f32(float v) { return v; }
+  __device__ static float from_f32(float v) { return v; }
+};
+template <> struct Store<f16> {
+  __device__ static float to_f32(f16 v) { return (float)v; }
+  __device__ static f16 from_f32(float v) { return (f16)v; }
+};
+template <> struct Store<bf16_t> {
+  __device__ static float to_f32(bf16_t v) { return bf16_to_f32(v); }
+  __device__ static bf16_t from_f32(float v) { return f32_to_bf16(v); }
+};
+
+// ------------------------------------------------------------- reductions
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// --------------------------------------------------------------- host side
+inline size_t dtype_size(int dt) {
+  return dt == DION3_F32 ? 4 : (dt == DION3_F16 || dt == DION3_BF16) ? 2 : 0;
+}
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Per-kernel event timing (measurement only; see dion3_timing_enable).
+void timing_begin(const char* name, hipStream_t s);
+void timing_end(hipStream_t s);
+
+struct TimedLaunch {
+  hipStream_t s;
+  TimedLaunch(const char* name, hipStream_t st) : s(st) { timing_begin(name, s); }
+  ~TimedLaunch() { timing_end(s); }
+};
+
+inline int launch_status() {
+  return hipGetLastError() == hipSuccess ? DION3_OK : DION3_ERR_HIP;
+}
+
+inline bool canonical_dims(const dion3_group* g, int* n, int* m, int* axis) {
+  if (!g || g->rows <= 0 || g->cols <= 0 || g->batch <= 0) return false;
+  if ((long long)g->rows * g->cols > g->batch_stride && g->batch > 1) return false;
+  int ax = g->sel_axis;
+  if (ax != 0 && ax != 1) {
+    if (ax != -1) return false;
+    ax = g->rows <= g->cols ? 0 : 1;
+  }
+  *axis = ax;
+  *n = ax == 0 ? g->rows : g->cols;
+  *m = ax == 0 ? g->cols : g->rows;
+  return true;
+}
+
+// ------------------------------------------------- GEMM launchers (gemm.hip)
+enum GemmOp { OP_SYRK = 0, OP_SQ_ADD = 1, OP_SYM_MUL = 2, OP_GEMM = 3 };
+
+struct GemmArgs {
+  int op;
+  int dtype;          // operand dtype
+  int out_dtype;      // result dtype
+  int batch;
+  int M, N, K;        // C is M x N; contraction length K
+  const void* A; long long lda, sA;
+  const void* B; long long ldb, sB;     // B operand (K-contiguous rows, or X for OP_GEMM)
+  const void* E; long long lde, sE;     // epilogue operand (beta term), may be null
+  void* C; long long ldc, sC;
+  float alpha, beta, gamma;
+};
+
+int launch_gemm(const GemmArgs& a, hipStream_t s);
+
+}  // namespace dion3

@@ -1,0 +1,186 @@
+// Host driver of Gram Newton-Schulz and the C entry points of the symmetric
+// building blocks.
+//
+// Method: "Dion3: Full-Stack Orthogonal Updates", Section 4.  Gram
+// Newton-Schulz iterates on the Gram matrix R = X X^T instead of X:
+//   Z_t = a_t I + b_t R + c_t R^2        (one "A^2 + B" product)
+//   Q_t = Q_{t-1} Z_t                    (free on a pass's first iteration)
+//   R_t = Z_t R_{t-1} Z_t                (skipped on a pass's last iteration)
+// and multiplies back once, X <- Q X, at the end of a pass.  A restart after
+// iteration 2 starts a new pass on the current X (Gram matrix rebuilt, Q reset
+// to the identity), which keeps spurious negative eigenvalues of R in check in
+// half precision.  Every k x k product is a polynomial in the same Gram matrix,
+// so it is symmetric in exact arithmetic and is computed as a lower triangle
+// and mirrored (Section 5).
+//
+// Buffers: the k x m input X0 is read only; the pass outputs alternate between
+// a k x m workspace slice and O so that the last pass writes O; four k x k
+// workspace slices rotate between R, Z, Q and the Z R intermediate.
+#include "common.h"
+
+namespace dion3 {
+
+static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+static int sym_op(int op, int batch, int n, int K, int dtype, const void* A, long long sA,
+                  const void* B, long long sB, const void* E, long long sE, void* C, long long sC,
+                  float alpha, float beta, float gamma, hipStream_t s) {
+  GemmArgs g;
+  g.op = op; g.dtype = dtype; g.out_dtype = dtype; g.batch = batch;
+  g.M = n; g.N = n; g.K = K;
+  g.A = A; g.lda = K; g.sA = sA;
+  g.B = B; g.ldb = K; g.sB = sB;
+  g.E = E; g.lde = n; g.sE = sE;
+  g.C = C; g.ldc = n; g.sC = sC;
+  g.alpha = alpha; g.beta = beta; g.gamma = gamma;
+  return launch_gemm(g, s);
+}
+
+static int qx_op(int batch, int k, int m, int in_dtype, const void* Q, long long sQ, const void* X,
+                 long long sX, int out_dtype, void* Y, long long sY, float alpha, hipStream_t s) {
+  GemmArgs g;
+  g.op = OP_GEMM; g.dtype = in_dtype; g.out_dtype = out_dtype; g.batch = batch;
+  g.M = k; g.N = m; g.K = k;
+  g.A = Q; g.lda = k; g.sA = sQ;
+  g.B = X; g.ldb = m; g.sB = sX;
+  g.E = nullptr; g.lde = 0; g.sE = 0;
+  g.C = Y; g.ldc = m; g.sC = sY;
+  g.alpha = alpha; g.beta = 0.f; g.gamma = 0.f;
+  return launch_gemm(g, s);
+}
+
+static bool ns_dtype_ok(int dt) { return dt == DION3_F16 || dt == DION3_F32 || dt == DION3_BF16; }
+
+}  // namespace dion3
+
+using namespace dion3;
+
+extern "C" int dion3_syrk(int batch, int n, int kdim, int dtype, const void* A, long long strideA,
+                          void* C, long long strideC, float alpha, float beta, void* stream) {
+  if (batch < 1 || n < 1 || kdim < 1 || !A || !C || !ns_dtype_ok(dtype)) return DION3_ERR_INVALID_ARG;
+  if (A == C) return DION3_ERR_INVALID_ARG;
+  if (batch > 1 && (strideA < (long long)n * kdim || strideC < (long long)n * n)) return DION3_ERR_INVALID_ARG;
+  return sym_op(OP_SYRK, batch, n, kdim, dtype, A, strideA, A, strideA, beta != 0.f ? C : nullptr,
+                strideC, C, strideC, alpha, beta, 0.f, (hipStream_t)stream);
+}
+
+extern "C" int dion3_sym_sq_add(int batch, int n, int dtype, const void* A, long long strideA,
+                                const void* B, long long strideB, void* C, long long strideC,
+                                float alpha, float beta, float gamma, void* stream) {
+  if (batch < 1 || n < 1 || !A || !B || !C || !ns_dtype_ok(dtype)) return DION3_ERR_INVALID_ARG;
+  if (C == A || C == B) return DION3_ERR_INVALID_ARG;
+  const long long nn = (long long)n * n;
+  if (batch > 1 && (strideA < nn || strideB < nn || strideC < nn)) return DION3_ERR_INVALID_ARG;
+  return sym_op(OP_SQ_ADD, batch, n, n, dtype, A, strideA, A, strideA, B, strideB, C, strideC, alpha,
+                beta, gamma, (hipStream_t)stream);
+}
+
+extern "C" int dion3_sym_mul(int batch, int n, int dtype, const void* A, long long strideA,
+                             const void* B, long long strideB, void* C, long long strideC,
+                             float alpha, void* stream) {
+  if (batch < 1 || n < 1 || !A || !B || !C || !ns_dtype_ok(dtype)) return DION3_ERR_INVALID_ARG;
+  if (C == A || C == B) return DION3_ERR_INVALID_ARG;
+  const long long nn = (long long)n * n;
+  if (batch > 1 && (strideA < nn || strideB < nn || strideC < nn)) return DION3_ERR_INVALID_ARG;
+  return sym_op(OP_SYM_MUL, batch, n, n, dtype, A, strideA, B, strideB, nullptr, 0, C, strideC, alpha,
+                0.f, 0.f, (hipStream_t)stream);
+}
+
+extern "C" int dion3_gemm(int batch, int k, int m, int in_dtype, const void* Q, long long strideQ,
+                          const void* X, long long strideX, int out_dtype, void* Y, long long strideY,
+                          float alpha, void* stream) {
+  if (batch < 1 || k < 1 || m < 1 || !Q || !X || !Y || !ns_dtype_ok(in_dtype)) return DION3_ERR_INVALID_ARG;
+  if (Y == Q || Y == X) return DION3_ERR_INVALID_ARG;
+  if (!(out_dtype == in_dtype || (in_dtype == DION3_F16 && out_dtype == DION3_F32)))
+    return DION3_ERR_INVALID_ARG;
+  if (batch > 1 && (strideQ < (long long)k * k || strideX < (long long)k * m || strideY < (long long)k * m))
+    return DION3_ERR_INVALID_ARG;
+  return qx_op(batch, k, m, in_dtype, Q, strideQ, X, strideX, out_dtype, Y, strideY, alpha,
+               (hipStream_t)stream);
+}
+
+extern "C" size_t dion3_gram_ns_workspace_bytes(int batch, int k, int m, int ns_dtype) {
+  if (batch < 1 || k < 1 || m < 1 || !ns_dtype_ok(ns_dtype)) return 0;
+  const size_t es = dtype_size(ns_dtype);
+  return align256((size_t)batch * k * m * es) + 4 * align256((size_t)batch * k * k * es);
+}
+
+extern "C" int dion3_gram_ns(int batch, int k, int m, const dion3_ns_params* p, const void* X0,
+                             void* O, void* ws, size_t ws_bytes, void* stream) {
+  if (batch < 1 || k < 1 || m < 1 || k > m || !p || !X0 || !O || X0 == O) return DION3_ERR_INVALID_ARG;
+  if (p->T < 1 || !p->coeffs || !ns_dtype_ok(p->ns_dtype)) return DION3_ERR_INVALID_ARG;
+  for (int i = 0; i < 3 * p->T; ++i)
+    if (!(p->coeffs[i] == p->coeffs[i])) return DION3_ERR_INVALID_ARG;
+  const size_t need = dion3_gram_ns_workspace_bytes(batch, k, m, p->ns_dtype);
+  if (!ws || ws_bytes < need) return DION3_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const int dt = p->ns_dtype;
+  const size_t es = dtype_size(dt);
+  const long long skm = (long long)k * m, skk = (long long)k * k;
+  char* w = (char*)ws;
+  void* X2 = w;
+  void* sq[4];
+  char* base = w + align256((size_t)batch * skm * es);
+  for (int i = 0; i < 4; ++i) sq[i] = base + i * align256((size_t)batch * skk * es);
+
+  // iteration boundaries of the passes
+  int bounds[66];
+  int nb = 0;
+  bounds[nb++] = 0;
+  for (int t = 1; t < p->T && t < 64; ++t)
+    if ((p->restart_mask >> t) & 1u) bounds[nb++] = t;
+  bounds[nb++] = p->T;
+  const int npass = nb - 1;
+
+  bool used[4] = {false, false, false, false};
+  auto take = [&]() -> int {
+    for (int i = 0; i < 4; ++i)
+      if (!used[i]) { used[i] = true; return i; }
+    return -1;
+  };
+  auto give = [&](int i) { if (i >= 0) used[i] = false; };
+
+  const void* cur = X0;
+  int st = DION3_OK;
+  for (int ps = 0; ps < npass && st == DION3_OK; ++ps) {
+    const int t0 = bounds[ps], t1 = bounds[ps + 1];
+    void* out = ((npass - 1 - ps) % 2 == 0) ? O : X2;
+    const int R = take();
+    st = sym_op(OP_SYRK, batch, k, m, dt, cur, skm, cur, skm, nullptr, 0, sq[R], skk, 1.f, 0.f, 0.f, s);
+    int Q = -1;
+    for (int t = t0; t < t1 && st == DION3_OK; ++t) {
+      const float a = (float)p->coeffs[3 * t + 0];
+      const float b = (float)p->coeffs[3 * t + 1];
+      const float c = (float)p->coeffs[3 * t + 2];
+      const int Z = take();
+      st = sym_op(OP_SQ_ADD, batch, k, k, dt, sq[R], skk, sq[R], skk, sq[R], skk, sq[Z], skk, c, b, a, s);
+      if (st) break;
+      if (Q < 0) {
+        Q = Z;
+      } else {
+        const int Qn = take();
+        st = sym_op(OP_SYM_MUL, batch, k, k, dt, sq[Q], skk, sq[Z], skk, nullptr, 0, sq[Qn], skk, 1.f, 0.f,
+                    0.f, s);
+        give(Q);
+        Q = Qn;
+        if (st) break;
+      }
+      if (t < t1 - 1) {
+        const int P = take();
+        st = sym_op(OP_SYM_MUL, batch, k, k, dt, sq[Z], skk, sq[R], skk, nullptr, 0, sq[P], skk, 1.f, 0.f,
+                    0.f, s);
+        if (!st)
+          st = sym_op(OP_SYM_MUL, batch, k, k, dt, sq[P], skk, sq[Z], skk, nullptr, 0, sq[R], skk, 1.f, 0.f,
+                      0.f, s);
+        give(P);
+      }
+      if (Z != Q) give(Z);
+    }
+    if (st) break;
+    st = qx_op(batch, k, m, dt, sq[Q], skk, cur, skm, dt, out, skm, 1.f, s);
+    give(Q);
+    give(R);
+    cur = out;
+  }
+  return st;
+}

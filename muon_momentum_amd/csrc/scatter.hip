@@ -1,0 +1,315 @@
+// Gather of the selected lines into the Newton-Schulz input, and the fused
+// update of W and M.
+//
+// Method: "Dion3: Full-Stack Orthogonal Updates".
+//   Section 2: the Newton-Schulz input is normalised by its Frobenius norm so
+//   that every singular value lies in [0, 1].
+//   Section 6: W[S,:] <- W[S,:] - eta O with weight decay (if on) applied to
+//   all rows first; the whole update is evaluated in fp32 and cast back to the
+//   storage type once (the pages fuse it for this reason); error feedback
+//   multiplies only the selected rows of M by mu.
+//
+// Row selection gathers and scatters whole rows (one wave per row, 16-byte
+// vectors).  Column selection goes through a 64 x 64 LDS tile so that the
+// canonical [k][m] buffers are read and written along m while the stored
+// matrix is addressed at the selected columns of each row.
+#include "common.h"
+
+namespace dion3 {
+
+template <typename T> struct Pack8;   // 8 elements as whole 16-byte vectors
+template <> struct Pack8<bf16_t> { union U { uint4 v[1]; bf16_t e[8]; }; };
+template <> struct Pack8<f16> { union U { uint4 v[1]; f16 e[8]; }; };
+template <> struct Pack8<float> { union U { uint4 v[2]; float e[8]; }; };
+
+template <typename T>
+__device__ __forceinline__ void load8(typename Pack8<T>::U& u, const T* p) {
+#pragma unroll
+  for (int w = 0; w < (int)(8 * sizeof(T) / 16); ++w) u.v[w] = ((const uint4*)p)[w];
+}
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const typename Pack8<T>::U& u) {
+#pragma unroll
+  for (int w = 0; w < (int)(8 * sizeof(T) / 16); ++w) ((uint4*)p)[w] = u.v[w];
+}
+
+// mu * m rounded once to the storage type (the product is exact in fp64).
+template <typename T> __device__ __forceinline__ T decay_round(float mu, T m);
+template <> __device__ __forceinline__ bf16_t decay_round<bf16_t>(float mu, bf16_t m) {
+  return f64_to_bf16((double)mu * (double)bf16_to_f32(m));
+}
+template <> __device__ __forceinline__ float decay_round<float>(float mu, float m) { return mu * m; }
+
+// w' = round(fp32(a - eta o)) with a = fp32(u w) when decaying, else w.
+template <typename T>
+__device__ __forceinline__ T update_w(T w, float o, float eta, float u, bool decay) {
+  float a = Store<T>::to_f32(w);
+  if (decay) a = u * a;
+  return Store<T>::from_f32(__builtin_fmaf(-eta, o, a));
+}
+
+__device__ __forceinline__ float nscale(const double* sqn, int b, float eps) {
+  return (float)(1.0 / (sqrt(sqn[b]) + (double)eps));
+}
+
+// ----------------------------------------------------------------- gather
+template <typename TS, typename TX, bool VEC>
+__global__ __launch_bounds__(256) void gather_rows_kernel(
+    const TS* __restrict__ M, long long bstride, int nlines, int cols, const int32_t* __restrict__ idx,
+    int k, const double* __restrict__ sqn, float eps, TX* __restrict__ X) {
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = blockIdx.x * 4 + wave;
+  if (i >= k) return;
+  const float sc = nscale(sqn, b, eps);
+  const int r = idx[(long long)b * k + i];
+  if (r < 0 || r >= nlines) return;
+  const TS* src = M + b * bstride + (long long)r * cols;
+  TX* dst = X + ((long long)b * k + i) * cols;
+  if (VEC) {
+    for (int c = lane * 8; c < cols; c += 64 * 8) {
+      typename Pack8<TS>::U a;
+      typename Pack8<TX>::U o;
+      load8<TS>(a, src + c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o.e[e] = Store<TX>::from_f32(Store<TS>::to_f32(a.e[e]) * sc);
+      store8<TX>(dst + c, o);
+    }
+  } else {
+    for (int c = lane; c < cols; c += 64)
+      dst[c] = Store<TX>::from_f32(Store<TS>::to_f32(src[c]) * sc);
+  }
+}
+
+// X[b][i][j] = M[b][j][idx[i]] * scale;  grid (m/64, k/64, batch)
+template <typename TS, typename TX>
+__global__ __launch_bounds__(256) void gather_cols_kernel(
+    const TS* __restrict__ M, long long bstride, int rows, int cols, const int32_t* __restrict__ idx,
+    int k, const double* __restrict__ sqn, float eps, TX* __restrict__ X) {
+  __shared__ float tile[64][65];
+  const int b = blockIdx.z;
+  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+  const int t = threadIdx.x;
+  const int il = t & 63;
+  const float sc = nscale(sqn, b, eps);
+  int col = i0 + il < k ? idx[(long long)b * k + i0 + il] : -1;
+  if (col >= cols) col = -1;
+  const TS* Mb = M + b * bstride;
+#pragma unroll 4
+  for (int s = 0; s < 16; ++s) {
+    const int jj = (t >> 6) + 4 * s;
+    const int j = j0 + jj;
+    float v = 0.f;
+    if (col >= 0 && j < rows) v = Store<TS>::to_f32(Mb[(long long)j * cols + col]);
+    tile[il][jj] = v * sc;
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int s = 0; s < 16; ++s) {
+    const int il2 = (t >> 6) + 4 * s;
+    const int jl = t & 63;
+    const int i = i0 + il2, j = j0 + jl;
+    if (i < k && j < rows) X[((long long)b * k + i) * rows + j] = Store<TX>::from_f32(tile[il2][jl]);
+  }
+}
+
+// ------------------------------------------------------------------ apply
+template <typename TS, typename TO, bool VEC>
+__global__ __launch_bounds__(256) void apply_rows_kernel(
+    TS* __restrict__ W, TS* __restrict__ M, long long bstride, int nlines, int cols,
+    const int32_t* __restrict__ idx, int k, const TO* __restrict__ O, long long ostride, float eta,
+    float u, int decay, float mu) {
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = blockIdx.x * 4 + wave;
+  if (i >= k) return;
+  const int r = idx[(long long)b * k + i];
+  if (r < 0 || r >= nlines) return;
+  TS* w = W + b * bstride + (long long)r * cols;
+  TS* mm = M + b * bstride + (long long)r * cols;
+  const TO* o = O + b * ostride + (long long)i * cols;
+  if (VEC) {
+    for (int c = lane * 8; c < cols; c += 64 * 8) {
+      typename Pack8<TS>::U vw, vm;
+      typename Pack8<TO>::U vo;
+      load8<TS>(vw, w + c);
+      load8<TS>(vm, mm + c);
+      load8<TO>(vo, o + c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        vw.e[e] = update_w<TS>(vw.e[e], Store<TO>::to_f32(vo.e[e]), eta, u, decay != 0);
+        vm.e[e] = decay_round<TS>(mu, vm.e[e]);
+      }
+      store8<TS>(w + c, vw);
+      store8<TS>(mm + c, vm);
+    }
+  } else {
+    for (int c = lane; c < cols; c += 64) {
+      w[c] = update_w<TS>(w[c], Store<TO>::to_f32(o[c]), eta, u, decay != 0);
+      mm[c] = decay_round<TS>(mu, mm[c]);
+    }
+  }
+}
+
+// W[b][j][idx[i]] and M[b][j][idx[i]] for the canonical O[b][i][j]; grid (m/64, k/64, batch)
+template <typename TS, typename TO>
+__global__ __launch_bounds__(256) void apply_cols_kernel(
+    TS* __restrict__ W, TS* __restrict__ M, long long bstride, int rows, int cols,
+    const int32_t* __restrict__ idx, int k, const TO* __restrict__ O, long long ostride,
+    float eta, float u, int decay, float mu) {
+  __shared__ float tile[64][65];
+  const int b = blockIdx.z;
+  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+  const int t = threadIdx.x;
+  const TO* Ob = O + b * ostride;
+#pragma unroll 4
+  for (int s = 0; s < 16; ++s) {
+    const int il2 = (t >> 6) + 4 * s;
+    const int jl = t & 63;
+    const int i = i0 + il2, j = j0 + jl;
+    tile[il2][jl] = (i < k && j < rows) ? Store<TO>::to_f32(Ob[(long long)i * rows + j]) : 0.f;
+  }
+  __syncthreads();
+  const int il = t & 63;
+  const int col = i0 + il < k ? idx[(long long)b * k + i0 + il] : -1;
+  if (col < 0 || col >= cols) return;
+  TS* Wb = W + b * bstride;
+  TS* Mb = M + b * bstride;
+#pragma unroll 4
+  for (int s = 0; s < 16; ++s) {
+    const int jj = (t >> 6) + 4 * s;
+    const int j = j0 + jj;
+    if (j < rows) {
+      const long long off = (long long)j * cols + col;
+      Wb[off] = update_w<TS>(Wb[off], tile[il][jj], eta, u, decay != 0);
+      Mb[off] = decay_round<TS>(mu, Mb[off]);
+    }
+  }
+}
+
+// Weight decay of the unselected lines, W <- round(fp32(u w)) (only when wd != 0).
+template <typename TS>
+__global__ __launch_bounds__(256) void decay_unselected_kernel(
+    TS* __restrict__ W, long long bstride, int rows, int cols, int axis, int n,
+    const int32_t* __restrict__ idx, int k, float u) {
+  __shared__ uint32_t selmap[1024];   // n <= 32768 bits
+  const int b = blockIdx.y;
+  const int32_t* ib = idx + (long long)b * k;
+  for (int w = threadIdx.x; w < (n + 31) / 32; w += 256) selmap[w] = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < k; i += 256)
+    if (ib[i] >= 0 && ib[i] < n) atomicOr(&selmap[ib[i] >> 5], 1u << (ib[i] & 31));
+  __syncthreads();
+  TS* Wb = W + b * bstride;
+  // a work-group handles 8 stored rows
+  for (int rr = 0; rr < 8; ++rr) {
+    const int r = blockIdx.x * 8 + rr;
+    if (r >= rows) break;
+    if (axis == 0 && ((selmap[r >> 5] >> (r & 31)) & 1u)) continue;
+    TS* wr = Wb + (long long)r * cols;
+    for (int c = threadIdx.x; c < cols; c += 256) {
+      if (axis == 1 && ((selmap[c >> 5] >> (c & 31)) & 1u)) continue;
+      wr[c] = Store<TS>::from_f32(u * Store<TS>::to_f32(wr[c]));
+    }
+  }
+}
+
+// ------------------------------------------------------------------ host
+template <typename TS, typename TX>
+static void launch_gather(const dion3_group* g, int axis, int n, int m, const void* M,
+                          const int32_t* idx, int k, const double* sqn, float eps, void* X,
+                          hipStream_t s) {
+  TimedLaunch tl("gather_scale", s);
+  if (axis == 0) {
+    const bool vec = m % 8 == 0 && (g->batch == 1 || g->batch_stride % 8 == 0) && aligned16(M) &&
+                     aligned16(X);
+    dim3 grid((k + 3) / 4, g->batch);
+    if (vec)
+      hipLaunchKernelGGL((gather_rows_kernel<TS, TX, true>), grid, dim3(256), 0, s, (const TS*)M,
+                         g->batch_stride, n, m, idx, k, sqn, eps, (TX*)X);
+    else
+      hipLaunchKernelGGL((gather_rows_kernel<TS, TX, false>), grid, dim3(256), 0, s, (const TS*)M,
+                         g->batch_stride, n, m, idx, k, sqn, eps, (TX*)X);
+  } else {
+    dim3 grid((m + 63) / 64, (k + 63) / 64, g->batch);
+    hipLaunchKernelGGL((gather_cols_kernel<TS, TX>), grid, dim3(256), 0, s, (const TS*)M,
+                       g->batch_stride, g->rows, g->cols, idx, k, sqn, eps, (TX*)X);
+  }
+}
+
+template <typename TS, typename TO>
+static void launch_apply(const dion3_group* g, int axis, int n, int m, void* W, void* M,
+                         const int32_t* idx, int k, const void* O, long long ostride, float eta,
+                         float wd, float mu, hipStream_t s) {
+  // u = fp32(1 - eta wd): the product is exact in fp64, one rounding to fp32
+  const float u = (float)(1.0 - (double)eta * (double)wd);
+  const int decay = wd != 0.0f;
+  TimedLaunch tl("apply_update", s);
+  if (decay) {
+    dim3 grid((g->rows + 7) / 8, g->batch);
+    hipLaunchKernelGGL((decay_unselected_kernel<TS>), grid, dim3(256), 0, s, (TS*)W, g->batch_stride,
+                       g->rows, g->cols, axis, n, idx, k, u);
+  }
+  if (axis == 0) {
+    const bool vec = m % 8 == 0 && (g->batch == 1 || (g->batch_stride % 8 == 0 && ostride % 8 == 0)) &&
+                     aligned16(W) && aligned16(M) && aligned16(O);
+    dim3 grid((k + 3) / 4, g->batch);
+    if (vec)
+      hipLaunchKernelGGL((apply_rows_kernel<TS, TO, true>), grid, dim3(256), 0, s, (TS*)W, (TS*)M,
+                         g->batch_stride, n, m, idx, k, (const TO*)O, ostride, eta, u, decay, mu);
+    else
+      hipLaunchKernelGGL((apply_rows_kernel<TS, TO, false>), grid, dim3(256), 0, s, (TS*)W, (TS*)M,
+                         g->batch_stride, n, m, idx, k, (const TO*)O, ostride, eta, u, decay, mu);
+  } else {
+    dim3 grid((m + 63) / 64, (k + 63) / 64, g->batch);
+    hipLaunchKernelGGL((apply_cols_kernel<TS, TO>), grid, dim3(256), 0, s, (TS*)W, (TS*)M,
+                       g->batch_stride, g->rows, g->cols, idx, k, (const TO*)O, ostride, eta, u, decay,
+                       mu);
+  }
+}
+
+}  // namespace dion3
+
+using namespace dion3;
+
+extern "C" int dion3_gather_rows(const dion3_group* g, const void* M, const int32_t* idx, int k,
+                                 const double* sel_sqnorm, float eps, int x_dtype, void* X,
+                                 void* stream) {
+  int n, m, axis;
+  if (!canonical_dims(g, &n, &m, &axis)) return DION3_ERR_INVALID_ARG;
+  if (!M || !idx || !sel_sqnorm || !X || k < 1 || k > n || !(eps >= 0.f)) return DION3_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (g->dtype == DION3_BF16 && x_dtype == DION3_F16)
+    launch_gather<bf16_t, f16>(g, axis, n, m, M, idx, k, sel_sqnorm, eps, X, s);
+  else if (g->dtype == DION3_BF16 && x_dtype == DION3_F32)
+    launch_gather<bf16_t, float>(g, axis, n, m, M, idx, k, sel_sqnorm, eps, X, s);
+  else if (g->dtype == DION3_F32 && x_dtype == DION3_F32)
+    launch_gather<float, float>(g, axis, n, m, M, idx, k, sel_sqnorm, eps, X, s);
+  else if (g->dtype == DION3_F32 && x_dtype == DION3_F16)
+    launch_gather<float, f16>(g, axis, n, m, M, idx, k, sel_sqnorm, eps, X, s);
+  else
+    return DION3_ERR_INVALID_ARG;
+  return launch_status();
+}
+
+extern "C" int dion3_apply_rows(const dion3_group* g, void* W, void* M, const int32_t* idx, int k,
+                                const void* O, int o_dtype, long long o_stride, float eta, float wd,
+                                float mu, void* stream) {
+  int n, m, axis;
+  if (!canonical_dims(g, &n, &m, &axis)) return DION3_ERR_INVALID_ARG;
+  if (!W || !M || !idx || !O || k < 1 || k > n) return DION3_ERR_INVALID_ARG;
+  if (g->batch > 1 && o_stride < (long long)k * m) return DION3_ERR_INVALID_ARG;
+  if (n > 32768) return DION3_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  if (g->dtype == DION3_BF16 && o_dtype == DION3_F16)
+    launch_apply<bf16_t, f16>(g, axis, n, m, W, M, idx, k, O, o_stride, eta, wd, mu, s);
+  else if (g->dtype == DION3_BF16 && o_dtype == DION3_F32)
+    launch_apply<bf16_t, float>(g, axis, n, m, W, M, idx, k, O, o_stride, eta, wd, mu, s);
+  else if (g->dtype == DION3_F32 && o_dtype == DION3_F32)
+    launch_apply<float, float>(g, axis, n, m, W, M, idx, k, O, o_stride, eta, wd, mu, s);
+  else if (g->dtype == DION3_F32 && o_dtype == DION3_F16)
+    launch_apply<float, f16>(g, axis, n, m, W, M, idx, k, O, o_stride, eta, wd, mu, s);
+  else
+    return DION3_ERR_INVALID_ARG;
+  return launch_status();
+}

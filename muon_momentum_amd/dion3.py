@@ -1,0 +1,254 @@
+"""ctypes binding of libdion3.so: the C entry points under the same names.
+
+Argument marshalling only: torch tensors supply device pointers and the
+current HIP stream; every step of the optimizer runs in the library's kernels.
+Importing this module raises if the library has not been built, so a missing
+extension can never fall back to anything else.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdion3.so")
+
+F32, F16, BF16 = 0, 1, 2
+_TORCH_TO_DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+_DT_TO_TORCH = {v: k for k, v in _TORCH_TO_DT.items()}
+
+# Muon's published fixed quintic (a, b, c), used for every iteration unless a
+# table is given ("Dion3: Full-Stack Orthogonal Updates", Section 2 names the
+# coefficient sources but prints no values).
+DEFAULT_QUINTIC = (3.4445, -4.7750, 2.0315)
+DEFAULT_T = 5
+DEFAULT_RESTART_MASK = 1 << 2      # restart after iteration 2 (Section 4)
+DEFAULT_EPS = 1e-7
+
+
+class Dion3Error(RuntimeError):
+    pass
+
+
+class Group(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int), ("cols", ctypes.c_int), ("batch", ctypes.c_int),
+                ("batch_stride", ctypes.c_longlong), ("dtype", ctypes.c_int),
+                ("sel_axis", ctypes.c_int)]
+
+
+class NSParams(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int), ("coeffs", ctypes.POINTER(ctypes.c_double)),
+                ("restart_mask", ctypes.c_uint), ("eps", ctypes.c_float), ("ns_dtype", ctypes.c_int)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, ll, f, d, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_float,
+                           ctypes.c_double, ctypes.c_size_t)
+    gp = ctypes.POINTER(Group)
+    pp = ctypes.POINTER(NSParams)
+    sig = {
+        "dion3_k_from_fraction": (i, [i, d]),
+        "dion3_canonical": (i, [gp, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.POINTER(i)]),
+        "dion3_status_string": (ctypes.c_char_p, [i]),
+        "dion3_rowsel_workspace_bytes": (sz, [gp]),
+        "dion3_momentum_rowsel": (i, [gp, vp, vp, i, vp, vp, vp, vp, sz, vp]),
+        "dion3_gather_rows": (i, [gp, vp, vp, i, vp, f, i, vp, vp]),
+        "dion3_gram_ns_workspace_bytes": (sz, [i, i, i, i]),
+        "dion3_gram_ns": (i, [i, i, i, pp, vp, vp, vp, sz, vp]),
+        "dion3_syrk": (i, [i, i, i, i, vp, ll, vp, ll, f, f, vp]),
+        "dion3_sym_sq_add": (i, [i, i, i, vp, ll, vp, ll, vp, ll, f, f, f, vp]),
+        "dion3_sym_mul": (i, [i, i, i, vp, ll, vp, ll, vp, ll, f, vp]),
+        "dion3_gemm": (i, [i, i, i, i, vp, ll, vp, ll, i, vp, ll, f, vp]),
+        "dion3_apply_rows": (i, [gp, vp, vp, vp, i, vp, i, ll, f, f, f, vp]),
+        "dion3_step_workspace_bytes": (sz, [i, gp, ctypes.POINTER(i), pp]),
+        "dion3_step": (i, [i, gp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                           ctypes.POINTER(i), ctypes.POINTER(vp), pp, f, f, f, vp, sz, vp]),
+        "dion3_timing_enable": (i, [i]),
+        "dion3_timing_report": (i, [ctypes.c_char_p, sz]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+# ------------------------------------------------------------------ helpers
+def _check(status: int, what: str) -> None:
+    if status < 0:
+        raise Dion3Error(f"{what}: {lib.dion3_status_string(status).decode()} ({status})")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise Dion3Error("tensor must live on the GPU")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    return _TORCH_TO_DT[dt]
+
+
+def torch_dtype(code: int) -> torch.dtype:
+    return _DT_TO_TORCH[code]
+
+
+def make_group(t: torch.Tensor, sel_axis: int = -1) -> Group:
+    """Describe a [batch, rows, cols] tensor (rows and cols contiguous)."""
+    if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+        raise Dion3Error("group tensor must be [batch, rows, cols] with packed rows")
+    return Group(t.shape[1], t.shape[2], t.shape[0], t.stride(0), dtype_code(t.dtype), sel_axis)
+
+
+def make_ns_params(coeffs=None, T: int = DEFAULT_T, restart_mask: int = DEFAULT_RESTART_MASK,
+                   eps: float = DEFAULT_EPS, ns_dtype: int = F16):
+    """NSParams plus the ctypes array that keeps its coefficient table alive."""
+    if coeffs is None:
+        coeffs = [DEFAULT_QUINTIC] * T
+    flat = [float(v) for row in coeffs for v in row]
+    arr = (ctypes.c_double * len(flat))(*flat)
+    p = NSParams(len(coeffs), ctypes.cast(arr, ctypes.POINTER(ctypes.c_double)), restart_mask, eps, ns_dtype)
+    p._keep = arr
+    return p
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# -------------------------------------------------------------- entry points
+def dion3_k_from_fraction(n: int, f: float) -> int:
+    k = lib.dion3_k_from_fraction(n, f)
+    _check(k, "dion3_k_from_fraction")
+    return k
+
+
+def dion3_canonical(g: Group):
+    n, m, a = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(lib.dion3_canonical(ctypes.byref(g), ctypes.byref(n), ctypes.byref(m), ctypes.byref(a)),
+           "dion3_canonical")
+    return n.value, m.value, a.value
+
+
+def dion3_rowsel_workspace_bytes(g: Group) -> int:
+    return lib.dion3_rowsel_workspace_bytes(ctypes.byref(g))
+
+
+def dion3_momentum_rowsel(M, G, k, idx, keys=None, sel_sqnorm=None, ws=None, sel_axis=-1):
+    g = make_group(M, sel_axis)
+    if ws is None:
+        ws = workspace(dion3_rowsel_workspace_bytes(g), M.device)
+    _check(lib.dion3_momentum_rowsel(ctypes.byref(g), _ptr(M), _ptr(G), k, _ptr(idx), _ptr(keys),
+                                     _ptr(sel_sqnorm), _ptr(ws), ws.numel(), _stream()),
+           "dion3_momentum_rowsel")
+
+
+def dion3_gather_rows(M, idx, k, sel_sqnorm, X, eps=DEFAULT_EPS, sel_axis=-1):
+    g = make_group(M, sel_axis)
+    _check(lib.dion3_gather_rows(ctypes.byref(g), _ptr(M), _ptr(idx), k, _ptr(sel_sqnorm), eps,
+                                 dtype_code(X.dtype), _ptr(X), _stream()), "dion3_gather_rows")
+
+
+def dion3_gram_ns_workspace_bytes(batch, k, m, ns_dtype) -> int:
+    return lib.dion3_gram_ns_workspace_bytes(batch, k, m, ns_dtype)
+
+
+def dion3_gram_ns(X0, O, params=None, ws=None):
+    b, k, m = X0.shape
+    p = params if params is not None else make_ns_params(ns_dtype=dtype_code(X0.dtype))
+    if ws is None:
+        ws = workspace(dion3_gram_ns_workspace_bytes(b, k, m, p.ns_dtype), X0.device)
+    _check(lib.dion3_gram_ns(b, k, m, ctypes.byref(p), _ptr(X0), _ptr(O), _ptr(ws), ws.numel(),
+                             _stream()), "dion3_gram_ns")
+
+
+def dion3_syrk(A, C, alpha=1.0, beta=0.0):
+    b, n, kd = A.shape
+    _check(lib.dion3_syrk(b, n, kd, dtype_code(A.dtype), _ptr(A), A.stride(0), _ptr(C), C.stride(0),
+                          alpha, beta, _stream()), "dion3_syrk")
+
+
+def dion3_sym_sq_add(A, B, C, alpha=1.0, beta=1.0, gamma=0.0):
+    b, n, _ = A.shape
+    _check(lib.dion3_sym_sq_add(b, n, dtype_code(A.dtype), _ptr(A), A.stride(0), _ptr(B), B.stride(0),
+                                _ptr(C), C.stride(0), alpha, beta, gamma, _stream()), "dion3_sym_sq_add")
+
+
+def dion3_sym_mul(A, B, C, alpha=1.0):
+    b, n, _ = A.shape
+    _check(lib.dion3_sym_mul(b, n, dtype_code(A.dtype), _ptr(A), A.stride(0), _ptr(B), B.stride(0),
+                             _ptr(C), C.stride(0), alpha, _stream()), "dion3_sym_mul")
+
+
+def dion3_gemm(Q, X, Y, alpha=1.0):
+    b, k, m = X.shape
+    _check(lib.dion3_gemm(b, k, m, dtype_code(Q.dtype), _ptr(Q), Q.stride(0), _ptr(X), X.stride(0),
+                          dtype_code(Y.dtype), _ptr(Y), Y.stride(0), alpha, _stream()), "dion3_gemm")
+
+
+def dion3_apply_rows(W, M, idx, k, O, eta, wd, mu, sel_axis=-1):
+    g = make_group(W, sel_axis)
+    _check(lib.dion3_apply_rows(ctypes.byref(g), _ptr(W), _ptr(M), _ptr(idx), k, _ptr(O),
+                                dtype_code(O.dtype), O.stride(0), eta, wd, mu, _stream()),
+           "dion3_apply_rows")
+
+
+class StepPlan:
+    """Marshalled arguments of dion3_step for a fixed list of group tensors."""
+
+    def __init__(self, Ws, Ms, Gs, ks, idxs, params, sel_axes=None):
+        n = len(Ws)
+        sel_axes = sel_axes or [-1] * n
+        self.groups = (Group * n)(*[make_group(W, a) for W, a in zip(Ws, sel_axes)])
+        self.W = (ctypes.c_void_p * n)(*[W.data_ptr() for W in Ws])
+        self.M = (ctypes.c_void_p * n)(*[M.data_ptr() for M in Ms])
+        self.G = (ctypes.c_void_p * n)(*[G.data_ptr() for G in Gs])
+        self.k = (ctypes.c_int * n)(*ks)
+        self.idx = (ctypes.c_void_p * n)(*[t.data_ptr() for t in idxs])
+        self.params = params
+        self.n = n
+        self._keep = (Ws, Ms, Gs, idxs)
+        nbytes = lib.dion3_step_workspace_bytes(n, self.groups, self.k, ctypes.byref(params))
+        if nbytes == 0:
+            raise Dion3Error("dion3_step_workspace_bytes: invalid groups")
+        self.ws = workspace(nbytes, Ws[0].device)
+
+    def step(self, eta, wd, mu):
+        _check(lib.dion3_step(self.n, self.groups, self.W, self.M, self.G, self.k, self.idx,
+                              ctypes.byref(self.params), eta, wd, mu, _ptr(self.ws), self.ws.numel(),
+                              _stream()), "dion3_step")
+
+
+def dion3_step(Ws, Ms, Gs, ks, idxs, eta, wd, mu, params=None, sel_axes=None):
+    p = params if params is not None else make_ns_params()
+    StepPlan(Ws, Ms, Gs, ks, idxs, p, sel_axes).step(eta, wd, mu)
+
+
+def dion3_timing_enable(max_launches: int) -> None:
+    _check(lib.dion3_timing_enable(max_launches), "dion3_timing_enable")
+
+
+def dion3_timing_report() -> dict:
+    buf = ctypes.create_string_buffer(1 << 16)
+    nb = lib.dion3_timing_report(buf, len(buf))
+    _check(nb, "dion3_timing_report")
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, cnt, ms = line.split()
+        out[name] = (int(cnt), float(ms))
+    return out

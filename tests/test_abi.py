@@ -1,0 +1,129 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol,
+computes its host-side helpers correctly and rejects invalid arguments before
+launching anything (none of these calls reaches the GPU)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dion3.h")
+
+d = pytest.importorskip("muon_momentum_amd.dion3")
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dion3_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared()
+    assert len(names) >= 15
+    out = subprocess.run(["nm", "-D", "--defined-only", d.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(dion3_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(d.lib, n)
+
+
+def test_k_from_fraction_matches_oracle():
+    rng = np.random.default_rng(1)
+    cases = [(10, 0.25), (4096, 0.25), (2048, 0.125), (10, 0.7), (3, 1 / 3), (1, 1.0), (5120, 0.25),
+             (1000, 1e-12), (7, 0.1 * 3)]
+    cases += [(int(rng.integers(1, 40000)), float(rng.random()) or 0.5) for _ in range(2000)]
+    for n, f in cases:
+        assert d.dion3_k_from_fraction(n, f) == O.k_from_fraction(n, f), (n, f)
+    for n, f in [(0, 0.5), (10, 0.0), (10, 1.0000001), (10, float("nan")), (-1, 0.5)]:
+        assert d.lib.dion3_k_from_fraction(n, f) == -1
+
+
+def test_canonical_orientation():
+    for (r, c, ax, want) in [(4096, 4096, -1, (4096, 4096, 0)), (4096, 11008, -1, (4096, 11008, 0)),
+                             (11008, 4096, -1, (4096, 11008, 1)), (256, 1024, 1, (1024, 256, 1)),
+                             (300, 200, 0, (300, 200, 0))]:
+        g = d.Group(r, c, 2, r * c, d.BF16, ax)
+        assert d.dion3_canonical(g) == want
+        assert O.canonical_axis(r, c, ax) == want[2]
+    with pytest.raises(d.Dion3Error):
+        d.dion3_canonical(d.Group(0, 5, 1, 0, d.BF16, -1))
+    with pytest.raises(d.Dion3Error):
+        d.dion3_canonical(d.Group(5, 5, 2, 24, d.BF16, -1))   # stride < rows*cols
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def test_invalid_arguments_rejected_without_launch():
+    L = d.lib
+    g = d.Group(64, 128, 2, 64 * 128, d.BF16, -1)
+    gp = ctypes.byref(g)
+    need = L.dion3_rowsel_workspace_bytes(gp)
+    assert need >= 256
+    # k outside [1, n]
+    assert L.dion3_momentum_rowsel(gp, FAKE, FAKE, 0, FAKE, None, None, FAKE, need, None) == -1
+    assert L.dion3_momentum_rowsel(gp, FAKE, FAKE, 65, FAKE, None, None, FAKE, need, None) == -1
+    # null tensors
+    assert L.dion3_momentum_rowsel(gp, None, FAKE, 4, FAKE, None, None, FAKE, need, None) == -1
+    # workspace too small
+    assert L.dion3_momentum_rowsel(gp, FAKE, FAKE, 4, FAKE, None, None, FAKE, need - 1, None) == -3
+    # unsupported storage dtype
+    g16 = d.Group(64, 128, 2, 64 * 128, d.F16, -1)
+    assert L.dion3_momentum_rowsel(ctypes.byref(g16), FAKE, FAKE, 4, FAKE, None, None, FAKE, need, None) == -1
+    # n beyond the top-k limit
+    big = d.Group(40000, 40000, 1, 40000 * 40000, d.BF16, -1)
+    nb = L.dion3_rowsel_workspace_bytes(ctypes.byref(big))
+    assert L.dion3_momentum_rowsel(ctypes.byref(big), FAKE, FAKE, 4, FAKE, None, None, FAKE, nb, None) == -2
+    # gather / apply
+    assert L.dion3_gather_rows(gp, FAKE, FAKE, 0, FAKE, 1e-7, d.F16, FAKE, None) == -1
+    assert L.dion3_gather_rows(gp, FAKE, FAKE, 4, FAKE, 1e-7, d.BF16, FAKE, None) == -1
+    assert L.dion3_apply_rows(gp, FAKE, FAKE, FAKE, 4, FAKE, d.BF16, 4 * 128, 0.1, 0.0, 0.9, None) == -1
+    assert L.dion3_apply_rows(gp, FAKE, FAKE, FAKE, 4, FAKE, d.F16, 3 * 128, 0.1, 0.0, 0.9, None) == -1
+    # symmetric building blocks: aliasing, sizes, dtypes, strides
+    assert L.dion3_syrk(1, 64, 128, d.F16, FAKE, 0, FAKE, 0, 1.0, 0.0, None) == -1      # A == C
+    assert L.dion3_syrk(2, 64, 128, d.F16, FAKE, 10, ctypes.c_void_p(0x2000), 4096, 1.0, 0.0, None) == -1
+    assert L.dion3_syrk(1, 0, 128, d.F16, FAKE, 0, ctypes.c_void_p(0x2000), 0, 1.0, 0.0, None) == -1
+    assert L.dion3_syrk(1, 64, 128, 7, FAKE, 0, ctypes.c_void_p(0x2000), 0, 1.0, 0.0, None) == -1
+    assert L.dion3_sym_sq_add(1, 64, d.F16, FAKE, 0, FAKE, 0, FAKE, 0, 1.0, 1.0, 0.0, None) == -1
+    assert L.dion3_sym_mul(1, 64, d.F16, FAKE, 0, ctypes.c_void_p(0x2000), 0, FAKE, 0, 1.0, None) == -1
+    assert L.dion3_gemm(1, 64, 128, d.F16, FAKE, 0, ctypes.c_void_p(0x2000), 0, d.BF16,
+                        ctypes.c_void_p(0x3000), 0, 1.0, None) == -1
+    # gram_ns: k > m, bad params, workspace
+    p = d.make_ns_params()
+    pp = ctypes.byref(p)
+    wsn = L.dion3_gram_ns_workspace_bytes(2, 64, 128, d.F16)
+    assert wsn > 0
+    assert L.dion3_gram_ns(2, 129, 128, pp, FAKE, ctypes.c_void_p(0x2000), FAKE, wsn, None) == -1
+    assert L.dion3_gram_ns(2, 64, 128, pp, FAKE, ctypes.c_void_p(0x2000), FAKE, wsn - 1, None) == -3
+    assert L.dion3_gram_ns(2, 64, 128, pp, FAKE, FAKE, FAKE, wsn, None) == -1          # X0 == O
+    bad = d.make_ns_params(T=0, coeffs=[])
+    assert L.dion3_gram_ns(2, 64, 128, ctypes.byref(bad), FAKE, ctypes.c_void_p(0x2000), FAKE, wsn, None) == -1
+    # whole step: workspace query and a too-small workspace
+    groups = (d.Group * 2)(d.Group(64, 128, 2, 64 * 128, d.BF16, -1), d.Group(128, 64, 1, 128 * 64, d.BF16, -1))
+    ks = (ctypes.c_int * 2)(16, 16)
+    sw = L.dion3_step_workspace_bytes(2, groups, ks, pp)
+    assert sw > 0
+    ptrs = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    assert L.dion3_step(2, groups, ptrs, ptrs, ptrs, ks, ptrs, pp, 0.1, 0.0, 0.9, FAKE, sw - 1, None) == -3
+    ks_bad = (ctypes.c_int * 2)(16, 65)
+    assert L.dion3_step_workspace_bytes(2, groups, ks_bad, pp) == 0
+
+
+def test_status_strings():
+    for code in [0, -1, -2, -3, -4, 99]:
+        assert isinstance(d.lib.dion3_status_string(code), bytes)
+
+
+def test_gram_ns_workspace_formula():
+    L = d.lib
+    for (b, k, m, dt, es) in [(3, 100, 300, d.F16, 2), (1, 256, 1024, d.F32, 4)]:
+        al = lambda v: (v + 255) // 256 * 256
+        assert L.dion3_gram_ns_workspace_bytes(b, k, m, dt) == al(b * k * m * es) + 4 * al(b * k * k * es)

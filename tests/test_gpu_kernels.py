@@ -1,0 +1,268 @@
+"""GPU parity of each C entry point against the CPU oracle (through the C ABI).
+
+Sizes span several tiles and ragged tails; indices, M and the update rounding
+are compared bit for bit, floating-point products within tolerances derived
+from the arithmetic (fp32 accumulation, one rounding to the output type)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from helpers import bits, np_bits, rel_fro, to64
+from muon_momentum_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def d():
+    import muon_momentum_amd.dion3 as mod
+    return mod
+
+
+TD = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+# normwise tolerance for products stored in the output type (one rounding of
+# the result plus fp32 accumulation): well below the unit roundoff x 4
+TOL = {"f16": 2e-3, "bf16": 1.2e-2, "f32": 2e-5}
+
+
+# ------------------------------------------------------- symmetric products
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("b,n,kd", [(1, 256, 512), (3, 128, 1024), (2, 200, 300), (1, 384, 136), (1, 33, 7)])
+def test_syrk(d, dt, b, n, kd):
+    A = synth.dense(n, kd, b, dtype=dt, device=DEV, seed=n + kd)
+    C = torch.full((b, n, n), float("nan"), dtype=TD[dt], device=DEV)
+    d.dion3_syrk(A, C, alpha=1.0, beta=0.0)
+    torch.cuda.synchronize()
+    a = to64(A)
+    ref = a @ a.transpose(0, 2, 1)
+    got = to64(C)
+    assert np.all(np.isfinite(got))
+    cb = bits(C)
+    assert np.array_equal(cb, cb.transpose(0, 2, 1))       # exactly symmetric
+    assert rel_fro(got, ref) <= TOL[dt]
+
+
+@pytest.mark.parametrize("dt", ["f16", "f32"])
+def test_syrk_beta(d, dt):
+    b, n, kd = 2, 256, 256
+    A = synth.dense(n, kd, b, dtype=dt, device=DEV, seed=3)
+    C0 = synth.symmetric(n, b, dtype=dt, device=DEV, seed=4)
+    C = C0.clone()
+    d.dion3_syrk(A, C, alpha=0.5, beta=-2.0)
+    torch.cuda.synchronize()
+    a = to64(A)
+    ref = 0.5 * a @ a.transpose(0, 2, 1) - 2.0 * to64(C0)
+    assert rel_fro(to64(C), ref) <= TOL[dt]
+    cb = bits(C)
+    assert np.array_equal(cb, cb.transpose(0, 2, 1))
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("b,n", [(1, 256), (2, 384), (3, 200), (1, 130)])
+def test_sym_sq_add(d, dt, b, n):
+    A = synth.symmetric(n, b, dtype=dt, device=DEV, seed=10 + n)
+    B = synth.symmetric(n, b, dtype=dt, device=DEV, seed=20 + n)
+    C = torch.empty_like(A)
+    al, be, ga = 2.0315, -4.7750, 3.4445
+    d.dion3_sym_sq_add(A, B, C, alpha=al, beta=be, gamma=ga)
+    torch.cuda.synchronize()
+    a, bb = to64(A), to64(B)
+    ref = al * a @ a + be * bb + ga * np.eye(n)[None]
+    assert rel_fro(to64(C), ref) <= TOL[dt]
+    cb = bits(C)
+    assert np.array_equal(cb, cb.transpose(0, 2, 1))
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("b,n", [(1, 256), (2, 200)])
+def test_sym_mul_commuting(d, dt, b, n):
+    """A and B are polynomials in one symmetric matrix, so A B is symmetric."""
+    S = to64(synth.symmetric(n, b, dtype="f32", device="cpu", seed=5))
+    A64 = 1.5 * np.eye(n)[None] + 0.7 * S
+    B64 = 0.3 * np.eye(n)[None] - 0.2 * S + 0.4 * S @ S
+    A = torch.from_numpy(A64).to(TD[dt]).to(DEV)
+    B = torch.from_numpy(B64).to(TD[dt]).to(DEV)
+    C = torch.empty_like(A)
+    d.dion3_sym_mul(A, B, C, alpha=1.0)
+    torch.cuda.synchronize()
+    a, bb = to64(A), to64(B)
+    ref = a @ bb
+    ref = np.tril(ref) + np.tril(ref, -1).transpose(0, 2, 1)   # the lower triangle, mirrored
+    assert rel_fro(to64(C), ref) <= TOL[dt]
+    cb = bits(C)
+    assert np.array_equal(cb, cb.transpose(0, 2, 1))
+
+
+@pytest.mark.parametrize("dt,odt", [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("f32", "f32")])
+@pytest.mark.parametrize("b,k,m", [(1, 256, 1024), (2, 128, 640), (2, 100, 300), (1, 64, 2048)])
+def test_gemm_qx(d, dt, odt, b, k, m):
+    Q = synth.symmetric(k, b, dtype=dt, device=DEV, seed=k)
+    X = synth.dense(k, m, b, dtype=dt, device=DEV, seed=m)
+    Y = torch.empty(b, k, m, dtype=TD[odt], device=DEV)
+    d.dion3_gemm(Q, X, Y, alpha=1.0)
+    torch.cuda.synchronize()
+    ref = to64(Q) @ to64(X)
+    assert rel_fro(to64(Y), ref) <= TOL[odt if odt != "f32" else dt]
+
+
+# --------------------------------------------------- momentum and selection
+def _rowsel_case(d, rows, cols, batch, dt, k, sel_axis=-1, G=None, M0=None):
+    if G is None:
+        G = synth.gradient(rows, cols, batch, dtype=dt, device=DEV, group_seed=rows + cols, sel_axis=sel_axis)
+    M = (M0.clone() if M0 is not None
+         else synth.gradient(rows, cols, batch, dtype=dt, device=DEV, group_seed=7, step=3, sel_axis=sel_axis))
+    Mh, Gh = to64(M), to64(G)
+    n, m, axis = d.dion3_canonical(d.make_group(M, sel_axis))
+    idx = torch.full((batch, k), -1, dtype=torch.int32, device=DEV)
+    keys = torch.empty(batch, n, dtype=torch.float64, device=DEV)
+    sqn = torch.empty(batch, dtype=torch.float64, device=DEV)
+    d.dion3_momentum_rowsel(M, G, k, idx, keys, sqn, sel_axis=sel_axis)
+    torch.cuda.synchronize()
+    return M, Mh, Gh, idx.cpu().numpy(), keys.cpu().numpy(), sqn.cpu().numpy(), axis
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,cols,batch,f,axis", [
+    (256, 1024, 1, 1.0, -1), (300, 1000, 2, 0.25, -1), (200, 1001, 2, 0.125, -1),
+    (600, 200, 2, 0.25, -1), (1100, 520, 1, 0.5, -1), (2500, 2600, 1, 0.25, -1),
+    (257, 300, 3, 0.25, 1), (64, 64, 4, 0.5, -1)])
+def test_momentum_rowsel(d, dt, rows, cols, batch, f, axis):
+    n = (rows if rows <= cols else cols) if axis == -1 else (rows if axis == 0 else cols)
+    k = O.k_from_fraction(n, f)
+    M, Mh, Gh, idx, keys, sqn, ax = _rowsel_case(d, rows, cols, batch, dt, k, sel_axis=axis)
+    for b in range(batch):
+        Mref = O.momentum_accumulate(Mh[b], Gh[b], dt)
+        assert np.array_equal(bits(M[b]), np_bits(Mref, TD[dt]))          # M bit-exact
+        Mc = Mref if ax == 0 else Mref.T
+        kref = O.l1_row_norms(Mc)
+        assert np.max(np.abs(keys[b] - kref) / np.maximum(kref, 1e-300)) <= 1e-12
+        sref = O.select_rows(kref, k)
+        # boundary gap: the k-th and (k+1)-th keys must be clearly separated
+        srt = np.sort(kref)[::-1]
+        if k < n:
+            assert (srt[k - 1] - srt[k]) / srt[k - 1] > 1e-12
+        assert np.array_equal(idx[b], sref)                                 # indices bit-exact
+        sq = float(np.sum(Mc[sref] ** 2))
+        assert abs(sqn[b] - sq) <= 1e-12 * sq
+
+
+def test_rowsel_ties_and_nan(d):
+    rows, cols = 40, 96
+    g = torch.zeros(1, rows, cols, dtype=torch.float32)
+    rng = np.random.default_rng(3)
+    base = rng.standard_normal(cols).astype(np.float32)
+    for r in [5, 9, 17, 30]:
+        g[0, r] = torch.from_numpy(base)           # four identical rows (equal keys)
+    g[0, 2] = torch.from_numpy(base * 0.5)
+    g[0, 33, 7] = float("nan")
+    G = g.to(DEV)
+    M0 = torch.zeros_like(G)
+    for k, want in [(1, [33]), (3, [5, 9, 33]), (5, [5, 9, 17, 30, 33]), (6, [2, 5, 9, 17, 30, 33]),
+                    (8, [0, 1, 2, 5, 9, 17, 30, 33])]:
+        _, _, _, idx, _, _, _ = _rowsel_case(d, rows, cols, 1, "f32", k, G=G, M0=M0)
+        assert list(idx[0]) == want, (k, idx[0])
+
+
+def test_rowsel_deterministic(d):
+    outs = []
+    for _ in range(2):
+        M, _, _, idx, keys, sqn, _ = _rowsel_case(d, 700, 300, 2, "bf16", 75)
+        outs.append((bits(M), idx, keys.view(np.int64), sqn.view(np.int64)))
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------------- gather
+@pytest.mark.parametrize("dt,xdt", [("bf16", "f16"), ("f32", "f32"), ("bf16", "f32")])
+@pytest.mark.parametrize("rows,cols,batch,f", [(256, 1024, 1, 1.0), (300, 1000, 2, 0.25), (600, 200, 2, 0.25),
+                                               (130, 77, 1, 0.5)])
+def test_gather(d, dt, xdt, rows, cols, batch, f):
+    n = min(rows, cols)
+    k = O.k_from_fraction(n, f)
+    M, Mh, Gh, idx, keys, sqn, ax = _rowsel_case(d, rows, cols, batch, dt, k)
+    m = cols if ax == 0 else rows
+    X = torch.empty(batch, k, m, dtype=TD[xdt], device=DEV)
+    d.dion3_gather_rows(M, torch.from_numpy(idx).to(DEV), k, torch.from_numpy(sqn).to(DEV), X, eps=1e-7)
+    torch.cuda.synchronize()
+    for b in range(batch):
+        Mc = to64(M[b]) if ax == 0 else to64(M[b]).T
+        ref = O.frobenius_normalize(Mc[idx[b]], 1e-7)
+        tol = 1e-3 if xdt == "f16" else 1e-6
+        assert rel_fro(to64(X[b]), ref) <= tol
+
+
+# -------------------------------------------------------------------- apply
+@pytest.mark.parametrize("dt,odt", [("bf16", "f16"), ("f32", "f32"), ("bf16", "f32")])
+@pytest.mark.parametrize("rows,cols,batch,f,wd", [(256, 1024, 1, 1.0, 0.0), (300, 1000, 2, 0.25, 0.0),
+                                                  (600, 200, 2, 0.25, 0.0), (300, 1000, 1, 0.25, 0.1),
+                                                  (600, 200, 1, 0.25, 0.1), (130, 77, 1, 0.5, 0.0)])
+def test_apply_rows_bit_exact(d, dt, odt, rows, cols, batch, f, wd):
+    n = min(rows, cols)
+    k = O.k_from_fraction(n, f)
+    ax = 0 if rows <= cols else 1
+    m = cols if ax == 0 else rows
+    W = synth.weights(rows, cols, batch, dtype=dt, device=DEV, group_seed=2)
+    M = synth.gradient(rows, cols, batch, dtype=dt, device=DEV, group_seed=5)
+    Ov = synth.dense(k, m, batch, dtype=odt, device=DEV, seed=9, std=0.03)
+    rng = np.random.default_rng(rows)
+    idx = np.stack([np.sort(rng.choice(n, k, replace=False)) for _ in range(batch)]).astype(np.int32)
+    Wh, Mh, Oh = to64(W), to64(M), to64(Ov)
+    eta, mu = 0.04, 0.95
+    d.dion3_apply_rows(W, M, torch.from_numpy(idx).to(DEV), k, Ov, eta, wd, mu)
+    torch.cuda.synchronize()
+    for b in range(batch):
+        Wc, Mc = (Wh[b], Mh[b]) if ax == 0 else (Wh[b].T, Mh[b].T)
+        Wr, Mr = O.apply_rows(Wc, Mc, idx[b], Oh[b], eta, wd, mu, dt)
+        if ax == 1:
+            Wr, Mr = Wr.T, Mr.T
+        assert np.array_equal(bits(W[b]), np_bits(Wr, TD[dt]))
+        assert np.array_equal(bits(M[b]), np_bits(Mr, TD[dt]))
+
+
+# ------------------------------------------------------- Gram Newton-Schulz
+@pytest.mark.parametrize("xdt,tol", [("f32", 1e-4), ("f16", 3e-2)])
+@pytest.mark.parametrize("b,k,m", [(1, 256, 1024), (2, 128, 512), (2, 100, 300), (1, 64, 64)])
+def test_gram_ns(d, xdt, tol, b, k, m):
+    rng = np.random.default_rng(k + m)
+    X = rng.standard_normal((b, k, m)) * np.exp(rng.standard_normal((b, k, 1)))
+    X0 = np.stack([O.frobenius_normalize(x, 1e-7) for x in X])
+    Xd = torch.from_numpy(X0).to(TD[xdt]).to(DEV)
+    Od = torch.empty_like(Xd)
+    params = d.make_ns_params(ns_dtype=d.dtype_code(TD[xdt]))
+    d.dion3_gram_ns(Xd, Od, params)
+    torch.cuda.synchronize()
+    xin = to64(Xd)
+    for i in range(b):
+        ref = O.ns_gram(xin[i], eps=0.0)   # input already normalised (up to its rounding)
+        err = rel_fro(to64(Od[i]), ref)
+        assert err <= tol, err
+        if xdt == "f16":
+            assert err <= 1e-2   # the fp16 storage model predicts about 1e-3
+
+
+def test_gram_ns_restart_variants(d):
+    b, k, m = 1, 128, 512
+    rng = np.random.default_rng(1)
+    X0 = O.frobenius_normalize(rng.standard_normal((k, m)) * np.exp(rng.standard_normal((k, 1))))
+    Xd = torch.from_numpy(X0[None]).float().to(DEV)
+    for mask, restart in [(0, ()), (1 << 2, (2,)), ((1 << 1) | (1 << 3), (1, 3)), ((1 << 1) | (1 << 2) | (1 << 3) | (1 << 4), (1, 2, 3, 4))]:
+        Od = torch.empty_like(Xd)
+        d.dion3_gram_ns(Xd, Od, d.make_ns_params(restart_mask=mask, ns_dtype=d.F32))
+        torch.cuda.synchronize()
+        ref = O.ns_gram(to64(Xd)[0], restart_after=restart, eps=0.0)
+        assert rel_fro(to64(Od)[0], ref) <= 1e-4, mask
+
+
+def test_gemm_deterministic(d):
+    A = synth.dense(512, 1024, 2, dtype="f16", device=DEV, seed=1)
+    outs = []
+    for _ in range(2):
+        C = torch.empty(2, 512, 512, dtype=torch.float16, device=DEV)
+        d.dion3_syrk(A, C)
+        torch.cuda.synchronize()
+        outs.append(bits(C))
+    assert np.array_equal(outs[0], outs[1])

@@ -1,0 +1,148 @@
+"""GPU parity of whole optimizer steps against the oracle.
+
+Small workload: one 256 x 1024 fp32 matrix, f = 1 (plain Muon through Gram
+Newton-Schulz with the restart), mu = 0.95, eta = 0.02, T = 5.  Plus a bf16
+multi-group step whose row- and column-selected groups share one
+Newton-Schulz batch."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from helpers import bits, np_bits, rel_fro, to64
+from muon_momentum_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TD = {"bf16": torch.bfloat16, "f32": torch.float32, "f16": torch.float16}
+
+
+@pytest.fixture(scope="module")
+def d():
+    import muon_momentum_amd.dion3 as mod
+    return mod
+
+
+def manual_step(d, groups, ks, params, eta, wd, mu):
+    """The step through the individual entry points; returns per-group idx and
+    the Newton-Schulz output O of every matrix (canonical orientation)."""
+    ns_t = d.torch_dtype(params.ns_dtype)
+    classes = {}
+    for gi, (W, M, G) in enumerate(groups):
+        n, m, ax = d.dion3_canonical(d.make_group(M))
+        classes.setdefault((ks[gi], m), []).append(gi)
+    idxs, Os = [None] * len(groups), [None] * len(groups)
+    for (k, m), members in classes.items():
+        nb = sum(groups[g][0].shape[0] for g in members)
+        X = torch.empty(nb, k, m, dtype=ns_t, device=DEV)
+        Ob = torch.empty_like(X)
+        off = 0
+        for g in members:
+            W, M, G = groups[g]
+            b = M.shape[0]
+            idx = torch.empty(b, k, dtype=torch.int32, device=DEV)
+            sqn = torch.empty(b, dtype=torch.float64, device=DEV)
+            d.dion3_momentum_rowsel(M, G, k, idx, None, sqn)
+            d.dion3_gather_rows(M, idx, k, sqn, X[off:off + b], eps=params.eps)
+            idxs[g] = idx
+            off += b
+        d.dion3_gram_ns(X, Ob, params)
+        off = 0
+        for g in members:
+            W, M, G = groups[g]
+            b = M.shape[0]
+            d.dion3_apply_rows(W, M, idxs[g], k, Ob[off:off + b], eta, wd, mu)
+            Os[g] = Ob[off:off + b].clone()
+            off += b
+    torch.cuda.synchronize()
+    return idxs, Os
+
+
+def test_config1_fp32_f1_three_steps(d):
+    rows, cols, T = 256, 1024, 5
+    mu, eta = 0.95, 0.02
+    W = synth.weights(rows, cols, 1, dtype="f32", device=DEV)
+    M = torch.zeros(1, rows, cols, dtype=torch.float32, device=DEV)
+    Wr, Mr = to64(W)[0], to64(M)[0]
+    params = d.make_ns_params(ns_dtype=d.F32)
+    k = d.dion3_k_from_fraction(rows, 1.0)
+    for step in range(3):
+        G = synth.gradient(rows, cols, 1, dtype="f32", device=DEV, step=step)
+        out = O.dion3_step(Wr, Mr, to64(G)[0], k=k, mu=mu, eta=eta, fmt="f32")
+        idxs, Os = manual_step(d, [(W, M, G)], [k], params, eta, 0.0, mu)
+        assert np.array_equal(idxs[0].cpu().numpy()[0], out["idx"])
+        assert np.array_equal(bits(M[0]), np_bits(out["M"], torch.float32))       # M bit-exact
+        Og = to64(Os[0])[0]
+        err = rel_fro(Og, out["O"])
+        assert err <= 1e-4, (step, err)
+        # W: the oracle's fused rounding applied to the GPU's own O is bit-exact
+        Wg_ref, _ = O.apply_rows(Wr, O.momentum_accumulate(Mr, to64(G)[0], "f32"), out["idx"], Og,
+                                 eta, 0.0, mu, "f32")
+        assert np.array_equal(bits(W[0]), np_bits(Wg_ref, torch.float32))
+        Wr, Mr = out["W"], out["M"]
+        # the GPU trajectory stays within tolerance of the oracle's
+        assert rel_fro(to64(W)[0] - to64(synth.weights(rows, cols, 1, dtype="f32", device=DEV))[0],
+                       Wr - to64(synth.weights(rows, cols, 1, dtype="f32", device=DEV))[0]) <= 1e-4
+
+
+def _groups(shapes, dt, step, seed0=0):
+    out = []
+    for gi, (r, c, b) in enumerate(shapes):
+        W = synth.weights(r, c, b, dtype=dt, device=DEV, group_seed=seed0 + gi)
+        M = synth.gradient(r, c, b, dtype=dt, device=DEV, group_seed=seed0 + gi + 50, step=99) * 0.5
+        M = M.to(TD[dt])
+        G = synth.gradient(r, c, b, dtype=dt, device=DEV, group_seed=seed0 + gi, step=step)
+        out.append((W, M, G))
+    return out
+
+
+@pytest.mark.parametrize("f", [0.25, 1.0])
+def test_multigroup_bf16_step_matches_manual_and_oracle(d, f):
+    shapes = [(128, 512, 3), (512, 128, 2), (256, 256, 2), (96, 200, 1)]
+    dt = "bf16"
+    mu, eta, wd = 0.95, 0.02 / f ** 0.5, 0.0
+    params = d.make_ns_params(ns_dtype=d.F16)
+    ks = [d.dion3_k_from_fraction(min(r, c), f) for r, c, _ in shapes]
+    A = _groups(shapes, dt, step=0)
+    B = [(W.clone(), M.clone(), G.clone()) for W, M, G in A]
+    host = [(to64(W), to64(M), to64(G)) for W, M, G in A]
+    # whole step in one call
+    idx_a = [torch.empty(b, k, dtype=torch.int32, device=DEV) for (_, _, b), k in zip(shapes, ks)]
+    d.dion3_step([g[0] for g in A], [g[1] for g in A], [g[2] for g in A], ks, idx_a, eta, wd, mu, params)
+    # the same through the individual entry points
+    idx_b, Os = manual_step(d, B, ks, params, eta, wd, mu)
+    for gi in range(len(shapes)):
+        assert np.array_equal(idx_a[gi].cpu().numpy(), idx_b[gi].cpu().numpy())
+        assert np.array_equal(bits(A[gi][0]), bits(B[gi][0]))
+        assert np.array_equal(bits(A[gi][1]), bits(B[gi][1]))
+    # oracle, matrix by matrix
+    for gi, (r, c, b) in enumerate(shapes):
+        Wh, Mh, Gh = host[gi]
+        for j in range(b):
+            out = O.dion3_step(Wh[j], Mh[j], Gh[j], k=ks[gi], mu=mu, eta=eta, fmt=dt)
+            assert np.array_equal(idx_b[gi].cpu().numpy()[j], out["idx"])
+            assert np.array_equal(bits(B[gi][1][j]), np_bits(out["M"], torch.bfloat16))
+            Og = to64(Os[gi][j])
+            assert rel_fro(Og, out["O"]) <= 3e-2
+            Mc = O.momentum_accumulate(Mh[j], Gh[j], dt)
+            ax = O.canonical_axis(r, c)
+            Wc, Mcc = (Wh[j], Mc) if ax == 0 else (Wh[j].T, Mc.T)
+            Wg, _ = O.apply_rows(Wc, Mcc, out["idx"], Og, eta, wd, mu, dt)
+            if ax == 1:
+                Wg = Wg.T
+            assert np.array_equal(bits(B[gi][0][j]), np_bits(Wg, torch.bfloat16))
+
+
+def test_step_deterministic(d):
+    shapes = [(256, 768, 2), (768, 256, 1)]
+    ks = [64, 64]
+    res = []
+    for _ in range(2):
+        A = _groups(shapes, "bf16", step=1, seed0=10)
+        idx = [torch.empty(b, k, dtype=torch.int32, device=DEV) for (_, _, b), k in zip(shapes, ks)]
+        d.dion3_step([g[0] for g in A], [g[1] for g in A], [g[2] for g in A], ks, idx, 0.04, 0.0, 0.95)
+        torch.cuda.synchronize()
+        res.append([bits(g[0]) for g in A] + [bits(g[1]) for g in A] + [i.cpu().numpy() for i in idx])
+    for a, b in zip(*res):
+        assert np.array_equal(a, b)
