@@ -1,0 +1,273 @@
+"""Benchmark of the Dion3 optimizer step on one MI355X.
+
+A step is one call of dion3_step over the 7B-like transformer shape set
+(32 layers x {4 x 4096x4096, 2 x 4096x11008, 1 x 11008x4096}, bf16 W, M, G):
+momentum accumulation with l1 keys, top-k selection (k = ceil(f n), f = 1/4 by
+default), gather and Frobenius scaling, Gram Newton-Schulz in fp16 (T = 5,
+restart after iteration 2) batched over same-shape selected submatrices, and
+the fused update of W with error feedback on M.  Inputs are synthetic and
+resident in HBM before the timed region starts; the momentum state carries
+across steps.
+
+Prints one JSON line: step milliseconds (the headline), the roofline of the
+kernel that takes the most time per step (algorithmic bytes or FLOPs per
+launch over its average launch duration, from HIP events recorded around every
+library launch during the timed steps), a per-kernel table, the symmetric-GEMM
+microbenchmark (C = A A^T and C = A^2 + B on n x n fp16/bf16) and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2516.6    # MI355X dense fp16 / bf16 MFMA
+MFMA_F32_PEAK_TFLOPS = 157.3     # MI355X fp32 matrix
+MU = 0.95
+ETA0 = 0.02                      # eta at f = 1; eta = ETA0 / sqrt(f)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--set", default="7b", choices=["1b", "7b", "14b"])
+    ap.add_argument("--f", type=float, default=0.25)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-microbench", action="store_true")
+    ap.add_argument("--copy-ref-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (a known-size "
+                         "reference for hardware byte counters)")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------ work accounting
+def kernel_work(groups, ks, ns_bytes=2, store_bytes=2):
+    """Algorithmic work per step of every kernel class of the library.
+
+    Bytes: momentum_keys reads M, G and writes M (3 x storage bytes per
+    parameter); gather_scale reads each selected element and writes it in the
+    Newton-Schulz type; apply_update reads and writes W and M and reads O per
+    selected element.  FLOPs: a symmetric product counts only its lower
+    triangle (k(k+1)/2 entries, 2 x contraction length each); Q X is a full
+    k x k by k x m product.  Returns {name: (kind, units per step)}."""
+    w = {"momentum_keys": 0.0, "topk_select": 0.0, "gather_scale": 0.0, "apply_update": 0.0,
+         "syrk": 0.0, "sym_sq_add": 0.0, "sym_mul": 0.0, "gemm_qx": 0.0}
+    for (rows, cols, b), k in zip(groups, ks):
+        n, m = min(rows, cols), max(rows, cols)
+        w["momentum_keys"] += b * rows * cols * 3 * store_bytes
+        w["topk_select"] += b * n * 8 * 2
+        w["gather_scale"] += b * k * m * (store_bytes + ns_bytes)
+        w["apply_update"] += b * k * m * (4 * store_bytes + ns_bytes)
+        tri = k * (k + 1) / 2
+        passes, iters = 2, 5                     # restart after iteration 2
+        w["syrk"] += b * passes * tri * 2 * m
+        w["sym_sq_add"] += b * iters * tri * 2 * k
+        # Q products: one per iteration except a pass's first (3); Z R Z: two
+        # products per iteration except a pass's last (3 iterations -> 6)
+        w["sym_mul"] += b * (3 + 6) * tri * 2 * k
+        w["gemm_qx"] += b * passes * 2 * k * k * m
+    kind = {"momentum_keys": "hbm", "topk_select": "hbm", "gather_scale": "hbm",
+            "apply_update": "hbm", "syrk": "mfma", "sym_sq_add": "mfma", "sym_mul": "mfma",
+            "gemm_qx": "mfma"}
+    return {name: (kind[name], v) for name, v in w.items()}
+
+
+def cpu_baseline(groups, ks, f, eta, set_name, budget_s=10.0, max_mats=4):
+    """The oracle's whole step on matrices of the first shape group (attention
+    projections) until about `budget_s` seconds have elapsed, scaled to the
+    full set by parameter count."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle as O
+    from muon_momentum_amd import synth
+
+    threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    rows, cols, b = groups[0]
+    k = ks[0]
+    spent, done = 0.0, 0
+    while done < min(b, max_mats) and (done == 0 or spent < budget_s):
+        W = synth.weights(rows, cols, 1, dtype="bf16", group_seed=1000 + done)[0]
+        G = synth.gradient(rows, cols, 1, dtype="bf16", group_seed=1000 + done, step=0)[0]
+        Wh = W.float().numpy().astype(np.float64)
+        Gh = G.float().numpy().astype(np.float64)
+        Mh = np.zeros_like(Gh)
+        t0 = time.perf_counter()
+        O.dion3_step(Wh, Mh, Gh, k=k, mu=MU, eta=eta, fmt="bf16")
+        spent += time.perf_counter() - t0
+        done += 1
+    params_sample = done * rows * cols
+    params_total = sum(r * c * bb for r, c, bb in groups)
+    per_step_s = spent * params_total / params_sample
+    return {"value": round(per_step_s * 1e3, 1), "unit": "ms per step (extrapolated)",
+            "cores": int(threads), "kind": "oracle",
+            "sample": (f"fp64 NumPy oracle, whole step on {done} of the {b} {rows}x{cols} matrices of "
+                       f"the {set_name} set at f={f:g} ({spent:.1f} s measured), scaled to the set's "
+                       f"{params_total / 1e9:.2f} G parameters by parameter count")}
+
+
+# ------------------------------------------------------------- the GPU parts
+def run_step_bench(d, synth, torch, args):
+    groups = synth.shape_groups(args.set)
+    dev = "cuda:0"
+    eta = ETA0 / math.sqrt(args.f)
+    ks = [d.dion3_k_from_fraction(min(r, c), args.f) for r, c, _ in groups]
+    Ws, Ms, Gs, idxs = [], [], [], []
+    for gi, (r, c, b) in enumerate(groups):
+        Ws.append(synth.weights(r, c, b, dtype="bf16", device=dev, group_seed=gi))
+        Gs.append(synth.gradient(r, c, b, dtype="bf16", device=dev, group_seed=gi, step=0))
+        Ms.append(torch.zeros(b, r, c, dtype=torch.bfloat16, device=dev))
+        idxs.append(torch.empty(b, ks[gi], dtype=torch.int32, device=dev))
+    params = d.make_ns_params(ns_dtype=d.F16)
+    plan = d.StepPlan(Ws, Ms, Gs, ks, idxs, params)
+    torch.cuda.synchronize()
+    print(f"# {args.set} set f={args.f:g}: groups {groups} k {ks}; workspace "
+          f"{plan.ws.numel() / 2**30:.2f} GiB", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        plan.step(eta, 0.0, MU)
+    torch.cuda.synchronize()
+    print("# warmup done", file=sys.stderr, flush=True)
+
+    launches_per_step = 64
+    d.dion3_timing_enable(launches_per_step * args.steps + 64)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        plan.step(eta, 0.0, MU)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    per_kernel = d.dion3_timing_report()
+    d.dion3_timing_enable(0)
+    print(f"# timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+
+    work = kernel_work(groups, ks)
+    table = {}
+    for name, (cnt, total_ms) in per_kernel.items():
+        kind, units = work.get(name, ("?", 0.0))
+        launches = cnt / args.steps
+        step_ms = total_ms / args.steps
+        avg_us = 1e3 * total_ms / cnt
+        if kind == "hbm":
+            ach = units / (step_ms * 1e-3) / 1e9
+            peak, unit = HBM_PEAK_GBS, "GB/s"
+        else:
+            ach = units / (step_ms * 1e-3) / 1e12
+            peak, unit = MFMA_F16_PEAK_TFLOPS, "TFLOP/s"
+        table[name] = {"launches_per_step": launches, "ms_per_step": round(step_ms, 4),
+                       "avg_launch_us": round(avg_us, 2), "bound": kind,
+                       "algorithmic_per_launch": units / launches if launches else 0.0,
+                       "achieved": round(ach, 2), "unit": unit, "frac": round(ach / peak, 4)}
+    del plan, Ws, Ms, Gs, idxs
+    torch.cuda.empty_cache()
+    return ms, table, groups, ks, eta
+
+
+def run_microbench(d, synth, torch):
+    """C = A A^T (n x n A) and C = A^2 + B (symmetric A, B), 10 warm-up and
+    50 timed launches each, timed with events on the launching stream."""
+    out = []
+    for dt in ("f16", "bf16"):
+        for n in (2048, 4096, 8192):
+            A = synth.dense(n, n, 1, dtype=dt, device="cuda:0", seed=1)
+            C = torch.empty(1, n, n, dtype=A.dtype, device="cuda:0")
+            S = synth.symmetric(n, 1, dtype=dt, device="cuda:0", seed=1)
+            B = synth.symmetric(n, 1, dtype=dt, device="cuda:0", seed=2)
+            for op in ("syrk", "sym_sq_add"):
+                fn = ((lambda: d.dion3_syrk(A, C)) if op == "syrk"
+                      else (lambda: d.dion3_sym_sq_add(S, B, C, 1.0, 1.0, 0.0)))
+                for _ in range(10):
+                    fn()
+                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                s.record()
+                for _ in range(50):
+                    fn()
+                e.record()
+                torch.cuda.synchronize()
+                us = 1e3 * s.elapsed_time(e) / 50
+                flop = n * n * (n + 1) + (n * (n + 1) / 2 if op == "sym_sq_add" else 0)
+                tf = flop / (us * 1e-6) / 1e12
+                out.append({"op": op, "n": n, "dtype": dt, "us": round(us, 2), "tflops": round(tf, 1),
+                            "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)})
+            del A, C, S, B
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (the step has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import muon_momentum_amd.dion3 as d      # raises if libdion3.so is missing
+    from muon_momentum_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    if args.copy_ref_mib > 0:
+        nb = args.copy_ref_mib << 20
+        src = torch.empty(nb, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"# copy reference: {args.copy_ref_mib} MiB read + written", file=sys.stderr, flush=True)
+        del src, dst
+
+    ms, table, groups, ks, eta = run_step_bench(d, synth, torch, args)
+    micro = [] if args.no_microbench else run_microbench(d, synth, torch)
+    if micro:
+        print("# microbench done", file=sys.stderr, flush=True)
+
+    dom = max(table, key=lambda k: table[k]["ms_per_step"])
+    t = table[dom]
+    roof = {"kernel": dom, "bound": t["bound"], "achieved": t["achieved"],
+            "peak": HBM_PEAK_GBS if t["bound"] == "hbm" else MFMA_F16_PEAK_TFLOPS,
+            "unit": t["unit"], "frac": t["frac"], "traffic": None,
+            "avg_launch_us": t["avg_launch_us"]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(groups, ks, args.f, eta, args.set)
+        print("# cpu baseline done", file=sys.stderr, flush=True)
+
+    line = {
+        "metric": "optimizer step ms (7B shape set, f=1/4) + sym-GEMM TFLOP/s vs MFMA peak",
+        "value": round(ms, 3), "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 storage, f16 Newton-Schulz",
+        "data": "synthetic (Gaussian gradients with log-normal line scales, seeded)",
+        "config": {"workload": f"{args.set} shape set Dion3 step, f={args.f:g}",
+                   "groups": [list(g) for g in groups], "k": ks, "T": 5, "restart_after": 2,
+                   "mu": MU, "eta": eta},
+        "roofline": roof,
+        "kernels": table,
+        "sym_gemm": micro,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -70,6 +70,7 @@ def test_config1_fp32_f1_three_steps(d):
     for step in range(3):
         G = synth.gradient(rows, cols, 1, dtype="f32", device=DEV, step=step)
         out = O.dion3_step(Wr, Mr, to64(G)[0], k=k, mu=mu, eta=eta, fmt="f32")
+        Wg_before = to64(W)[0]
         idxs, Os = manual_step(d, [(W, M, G)], [k], params, eta, 0.0, mu)
         assert np.array_equal(idxs[0].cpu().numpy()[0], out["idx"])
         assert np.array_equal(bits(M[0]), np_bits(out["M"], torch.float32))       # M bit-exact
@@ -77,7 +78,7 @@ def test_config1_fp32_f1_three_steps(d):
         err = rel_fro(Og, out["O"])
         assert err <= 1e-4, (step, err)
         # W: the oracle's fused rounding applied to the GPU's own O is bit-exact
-        Wg_ref, _ = O.apply_rows(Wr, O.momentum_accumulate(Mr, to64(G)[0], "f32"), out["idx"], Og,
+        Wg_ref, _ = O.apply_rows(Wg_before, O.momentum_accumulate(Mr, to64(G)[0], "f32"), out["idx"], Og,
                                  eta, 0.0, mu, "f32")
         assert np.array_equal(bits(W[0]), np_bits(Wg_ref, torch.float32))
         Wr, Mr = out["W"], out["M"]
