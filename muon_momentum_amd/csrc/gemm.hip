@@ -10,14 +10,16 @@
 // Layout: a work-group computes a BM x BN tile of C with 4 waves in a 2 x 2
 // arrangement.  Operand tiles are staged in LDS in a K-contiguous layout,
 // 128 bytes of K per row per stage, split in 16-byte chunks whose position is
-// XOR-swizzled by (row mod 8) so that 32 lanes reading one chunk column hit
-// distinct banks.  One MFMA step consumes two chunk columns: lanes 0-31 give
+// XOR-swizzled by the row so that the lanes of one LDS read phase reading a
+// chunk column hit distinct banks.  One MFMA step consumes two chunk columns: lanes 0-31 give
 // chunk 2s, lanes 32-63 chunk 2s+1 of rows (lane mod 32); the same assignment
 // on both operands makes the contraction exact for any chunk order.
 //   f16 / bf16: v_mfma_f32_32x32x16 (one MFMA per chunk pair)
 //   f32:        v_mfma_f32_32x32x2  (four MFMAs per chunk pair)
 // Accumulation is fp32; the epilogue applies alpha / beta / gamma in fp32 and
 // rounds once to the output type.
+#include <type_traits>
+
 #include "common.h"
 
 namespace dion3 {
@@ -64,8 +66,13 @@ struct KParams {
   int tiles_m, tiles_n, tiles_per_mat;
 };
 
+// LDS position of 16-byte chunk `chunk` of tile row `row`.  A 128-bit LDS read
+// is served 16 lanes (256 bytes, all 64 banks) at a time; 16 lanes reading one
+// chunk column of 16 consecutive rows must hit 16 distinct 16-byte slots.
+// Rows alternate between the two 128-byte halves of a 256-byte line, and
+// (row / 2) mod 8 permutes the chunk inside the half.
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * kRowBytes + ((chunk ^ (row & 7)) << 4);
+  return row * kRowBytes + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
 // Map a flat tile index to (ti, tj) with tj <= ti (lower triangle, diagonal included).
@@ -265,10 +272,295 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(KParams p) {
       }
 }
 
+
+// ---------------------------------------------------------------------------
+// Large-tile kernel for fp16 / bf16: a 256 x 256 tile per work-group, 4 waves
+// in 2 x 2, each wave owning a 128 x 128 block (4 x 4 MFMA 32x32x16 tiles), so
+// every 16-byte fragment read from LDS feeds four MFMAs.  A stage holds 64 K
+// elements (128 bytes per row) of both operands, 64 KB; two stages live in LDS.
+//
+// K-contiguous operands travel from global memory straight into LDS with
+// buffer loads that write LDS directly (each lane's 16 bytes land at the
+// wave's LDS base + 16 x lane), so no registers are spent on staging: lane L of
+// a wave instruction covering rows r0..r0+7 fetches row r = r0 + L/8, the chunk
+// whose swizzled position is L mod 8, which puts every chunk in its place.
+// The N-contiguous B operand of Q X is instead loaded as 8 x 8 element blocks
+// into registers and transposed there, so LDS is always written with 16-byte
+// K-contiguous chunks.  MFMA fragments are double-buffered across k-steps so
+// LDS latency overlaps the MFMAs of the previous step.
+// ---------------------------------------------------------------------------
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>{});
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8]) {
+  // in[r] holds elements (r, 0..7); out[c] receives elements (0..7, c)
+  uint32_t w[8][4];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    w[r][0] = in[r].x; w[r][1] = in[r].y; w[r][2] = in[r].z; w[r][3] = in[r].w;
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    uint32_t d[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t a = w[2 * q][c >> 1], b = w[2 * q + 1][c >> 1];
+      d[q] = (c & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+    }
+    out[c] = make_uint4(d[0], d[1], d[2], d[3]);
+  }
+}
+
+// Buffer resource (four scalar dwords) for raw loads of `bytes` bytes from
+// `base`; the last dword is the gfx9 raw-buffer format word.
+typedef int int4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ int4v make_rsrc(const void* base, long long bytes) {
+  const unsigned long long a = (unsigned long long)base;
+  int4v r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(a & 0xffffffffu));
+  r.y = __builtin_amdgcn_readfirstlane((int)(a >> 32) & 0xffff);    // stride 0
+  r.z = __builtin_amdgcn_readfirstlane(bytes > 0x7fffffffLL ? 0x7fffffff : (int)bytes);
+  r.w = 0x00020000;
+  return r;
+}
+
+// One wave instruction: 64 lanes x 16 bytes from rsrc at voffset + soffset
+// into LDS at `lds` (wave-uniform) + 16 x lane.  Issued from inline assembly
+// so that the compiler does not wait for it before unrelated LDS reads: the
+// caller waits (vmcnt) before the barrier that publishes the stage.
+__device__ __forceinline__ void lds_dma16(const int4v& rsrc, const void* lds, int voffset, int soffset) {
+  const int m0 = __builtin_amdgcn_readfirstlane((int)(unsigned)(uintptr_t)
+      (const __attribute__((address_space(3))) void*)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(m0), "v"(voffset), "s"(rsrc), "s"(soffset) : "memory", "m0");
+}
+
+template <typename T, typename TO, int OP>
+__global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm256_kernel(KParams p) {
+  constexpr bool SYM = OP != OP_GEMM;
+  constexpr bool BT = OP == OP_GEMM;
+  constexpr int BM = 256, BN = 256;
+  constexpr int BKE = kRowBytes / 2;          // 64 K elements per stage
+  constexpr int WT = 128;                     // wave tile edge
+  constexpr int SUB = WT / 32;                // 4 x 4 MFMA tiles per wave
+  constexpr int ROWS_PER_INSTR = 8;           // 1 KB = 8 LDS rows per wave instruction
+  constexpr int INSTR = BM / (4 * ROWS_PER_INSTR);   // 8 instructions per wave per operand
+
+  __shared__ __attribute__((aligned(1024))) char smem[2][2][BM * kRowBytes];
+
+  const int G = gridDim.x;
+  const int wg = blockIdx.x;
+  const int per = G / 8;
+  const int id = wg < per * 8 ? (wg % 8) * per + wg / 8 : wg;
+  const int bat = id / p.tiles_per_mat;
+  const int t = id % p.tiles_per_mat;
+  int ti, tj;
+  if (SYM) {
+    tri_index(t, ti, tj);
+  } else {
+    ti = t % p.tiles_m;
+    tj = t / p.tiles_m;
+  }
+  // the tile coordinates are uniform: keep them (and the buffer resources
+  // derived from them) in scalar registers
+  ti = __builtin_amdgcn_readfirstlane(ti);
+  tj = __builtin_amdgcn_readfirstlane(tj);
+  const int bu = __builtin_amdgcn_readfirstlane(bat);
+  const int m0 = ti * BM, n0 = tj * BN;
+
+  const T* A = (const T*)p.A + bu * p.sA;
+  const T* B = (const T*)p.B + bu * p.sB;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // direct-to-LDS addressing: this lane fetches row (wave*8 + lane/8) + 32 s of
+  // the tile, chunk (lane%8) ^ (lane/8); byte offsets relative to the tile origin
+  const int4v ra = make_rsrc(A, (long long)p.M * p.lda * 2);
+  const int lrow = wave * ROWS_PER_INSTR + (lane >> 3);
+  const int lchunk = (lane & 7) ^ ((lrow >> 1) & 7);   // rows r0 + 32 s keep (row/2) mod 8
+  const int va = ((m0 + lrow) * (int)p.lda + lchunk * 8) * 2;
+  const int rstep_a = 4 * ROWS_PER_INSTR * (int)p.lda * 2;   // 32 rows
+  const int4v rb = make_rsrc(B, BT ? (long long)p.K * p.ldb * 2 : (long long)p.N * p.ldb * 2);
+  const int vb = ((n0 + lrow) * (int)p.ldb + lchunk * 8) * 2;
+  const int rstep_b = 4 * ROWS_PER_INSTR * (int)p.ldb * 2;
+  // Q X: the N-contiguous B operand is read with ordinary buffer loads into
+  // registers (the compiler tracks them); this lane's 8 x 8 block starts at
+  // row 8 kb, column n0 + 8 nb of the stage
+  const __amdgpu_buffer_rsrc_t rbq = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(B), 0, (int)(BT ? min((long long)p.K * p.ldb * 2, 0x7fffffffLL) : 0), 0x00020000);
+  const int vbt = ((tid & 7) * 8 * (int)p.ldb + n0 + (tid >> 3) * 8) * 2;
+  (void)rb; (void)vb; (void)rstep_b; (void)rbq; (void)vbt;
+
+  floatx16 acc[SUB][SUB];
+#pragma unroll
+  for (int i = 0; i < SUB; ++i)
+#pragma unroll
+    for (int j = 0; j < SUB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  uint4 rbt[8];   // transposed-B staging (Q X only)
+
+  auto issue_stage = [&](int buf, int k0) {
+    char* sa = smem[buf][0] + wave * ROWS_PER_INSTR * kRowBytes;
+#pragma unroll
+    for (int s = 0; s < INSTR; ++s) lds_dma16(ra, sa + s * 4 * ROWS_PER_INSTR * kRowBytes, va, k0 * 2 + s * rstep_a);
+    if (!BT) {
+      char* sb = smem[buf][1] + wave * ROWS_PER_INSTR * kRowBytes;
+#pragma unroll
+      for (int s = 0; s < INSTR; ++s) lds_dma16(rb, sb + s * 4 * ROWS_PER_INSTR * kRowBytes, vb, k0 * 2 + s * rstep_b);
+    } else {
+      // an 8 (K) x 8 (N) block per thread (kb = tid mod 8, nb = tid / 8): rows
+      // k0 + 8 kb + r, columns n0 + 8 nb + c; eight consecutive lanes share
+      // nb, so each LDS write instruction fills whole 128-byte rows
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rbq, vbt, (k0 + r) * (int)p.ldb * 2, 0);
+        rbt[r] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
+    }
+  };
+  auto finish_stage = [&](int buf) {
+    if (BT) {
+      char* sb = smem[buf][1];
+      const int kb = tid & 7, nb = tid >> 3;
+      uint4 tr[8];
+      transpose8x8<T>(rbt, tr);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) *(uint4*)(sb + swz(nb * 8 + c, kb)) = tr[c];
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  const int KT = p.K / BKE;
+  issue_stage(0, 0);
+  finish_stage(0);
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < KT) issue_stage(cur ^ 1, (kt + 1) * BKE);
+    const char* sa = smem[cur][0];
+    const char* sb = smem[cur][1];
+    // every fragment of the stage gets its own registers (32 x 16 bytes per
+    // lane), so reads for the next k-step can be in flight during this one
+    constexpr int STEPS = kChunks / 2;
+    uint4 fa[STEPS][SUB], fb[STEPS][SUB];
+    static_for<STEPS>([&](auto sc) {
+      constexpr int st = decltype(sc)::value;
+      const int chunk = 2 * st + (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < SUB; ++i) fa[st][i] = *(const uint4*)(sa + swz(wm * WT + i * 32 + (lane & 31), chunk));
+#pragma unroll
+      for (int j = 0; j < SUB; ++j) fb[st][j] = *(const uint4*)(sb + swz(wn * WT + j * 32 + (lane & 31), chunk));
+    });
+    static_for<STEPS>([&](auto sc) {
+      constexpr int st = decltype(sc)::value;
+#pragma unroll
+      for (int i = 0; i < SUB; ++i)
+#pragma unroll
+        for (int j = 0; j < SUB; ++j) Mma<T>::run(acc[i][j], fa[st][i], fb[st][j]);
+    });
+    // schedule: step 0's reads, then each step's MFMAs with the next step's
+    // reads interleaved (one read per two MFMAs)
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * SUB, 0);
+    static_for<(STEPS - 1) * 2 * SUB>([&](auto) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    });
+    __builtin_amdgcn_sched_group_barrier(0x008, SUB * SUB, 0);
+    if (kt + 1 < KT) finish_stage(cur ^ 1);
+  }
+
+  // ---- epilogue: the lower triangle and its mirror; diagonal tiles write
+  // every entry exactly once (i >= j directly, i > j mirrored)
+  TO* C = (TO*)p.C + bu * p.sC;
+  const TO* E = (const TO*)p.E + (p.E ? bu * p.sE : 0);
+  const bool diag_tile = SYM && ti == tj;
+  if (diag_tile && wm < wn) return;            // the upper quadrant mirrors the lower one
+  constexpr bool HAS_E = OP == OP_SQ_ADD || OP == OP_SYRK;
+  const bool use_e = OP == OP_SQ_ADD || (OP == OP_SYRK && p.beta != 0.f);
+  // The epilogue operand is symmetric, so the four values E[gi..gi+3][gj] this
+  // lane needs per group are E[gj][gi..gi+3]: one 8-byte load.  All of them are
+  // issued before any store (the memory counter also counts stores).
+  uint2 epk[SUB][SUB][4];
+  if constexpr (HAS_E) {
+    if (use_e) {
+      static_for<SUB>([&](auto ic) {
+        static_for<SUB>([&](auto jc) {
+          constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
+          const int gi0 = m0 + wm * WT + i * 32;
+          const int gj0 = n0 + wn * WT + j * 32;
+          if (gi0 < gj0) return;
+          const int gj = gj0 + (lane & 31);
+          static_for<4>([&](auto gc) {
+            constexpr int g = decltype(gc)::value;
+            const int gib = gi0 + 8 * g + 4 * (lane >> 5);
+            epk[i][j][g] = *(const uint2*)(E + (long long)gj * p.lde + gib);
+          });
+        });
+      });
+    }
+  }
+  asm volatile("" ::: "memory");
+  static_for<SUB>([&](auto ic) {
+    static_for<SUB>([&](auto jc) {
+      constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
+      const int gi0 = m0 + wm * WT + i * 32;
+      const int gj0 = n0 + wn * WT + j * 32;
+      if (SYM && gi0 < gj0) return;            // above the diagonal (diagonal tiles only)
+      const bool below = !SYM || gi0 > gj0;    // whole 32 x 32 block strictly below
+      const int gj = gj0 + (lane & 31);
+      static_for<4>([&](auto gc) {
+        constexpr int g = decltype(gc)::value;
+        const int gib = gi0 + 8 * g + 4 * (lane >> 5);
+        union { uint2 u; TO e[4]; } ev;
+        if constexpr (HAS_E) ev.u = epk[i][j][g];
+        TO vv[4];
+        static_for<4>([&](auto qc) {
+          constexpr int q = decltype(qc)::value;
+          const int gi = gib + q;
+          float v = p.alpha * acc[i][j][4 * g + q];
+          if constexpr (HAS_E) {
+            if (use_e) v += p.beta * Store<TO>::to_f32(ev.e[q]);
+          }
+          if (OP == OP_SQ_ADD && gi == gj) v += p.gamma;
+          vv[q] = Store<TO>::from_f32(v);
+          if (below || gi >= gj) C[(long long)gi * p.ldc + gj] = vv[q];
+        });
+        if (SYM) {
+          if (below) {
+            // C[gj][gib .. gib+3]: four consecutive elements, one 8-byte store
+            union { uint2 u; TO e[4]; } pk;
+            static_for<4>([&](auto qc) { pk.e[decltype(qc)::value] = vv[decltype(qc)::value]; });
+            *(uint2*)(C + (long long)gj * p.ldc + gib) = pk.u;
+          } else {
+            static_for<4>([&](auto qc) {
+              constexpr int q = decltype(qc)::value;
+              if (gib + q > gj) C[(long long)gj * p.ldc + gib + q] = vv[q];
+            });
+          }
+        }
+      });
+    });
+  });
+}
+
 template <typename T, typename TO, int OP, int BM>
 static int launch_typed(const GemmArgs& a, hipStream_t s) {
   constexpr int BKE = kRowBytes / (int)sizeof(T);
   constexpr int EPC = Mma<T>::EPC;
+  constexpr bool HALF = sizeof(T) == 2;
   KParams p;
   p.M = a.M; p.N = a.N; p.K = a.K;
   p.A = a.A; p.lda = a.lda; p.sA = a.sA;
@@ -276,20 +568,36 @@ static int launch_typed(const GemmArgs& a, hipStream_t s) {
   p.E = a.E; p.lde = a.lde; p.sE = a.sE;
   p.C = a.C; p.ldc = a.ldc; p.sC = a.sC;
   p.alpha = a.alpha; p.beta = a.beta; p.gamma = a.gamma;
-  p.tiles_m = (a.M + BM - 1) / BM;
-  p.tiles_n = (a.N + BM - 1) / BM;
-  p.tiles_per_mat = OP == OP_GEMM ? p.tiles_m * p.tiles_n : p.tiles_m * (p.tiles_m + 1) / 2;
-  const long long grid = (long long)p.tiles_per_mat * a.batch;
+
+  // The 256 x 256 tile is used for fp16 / bf16 when the shape is a whole
+  // number of tiles and there are at least two tiles per compute unit;
+  // otherwise (ragged shapes, small batches, fp32) the 128 x 128 tile.
+  auto tiles_for = [&](int bm, int& tm, int& tn) {
+    tm = (a.M + bm - 1) / bm;
+    tn = (a.N + bm - 1) / bm;
+    return (long long)(OP == OP_GEMM ? tm * tn : tm * (tm + 1) / 2) * a.batch;
+  };
+  auto fast_for = [&](int bm) {
+    return a.M % bm == 0 && a.N % bm == 0 && a.K % BKE == 0 && a.lda % EPC == 0 &&
+           a.ldb % EPC == 0 && a.ldc % 8 == 0 && aligned16(a.A) && aligned16(a.B) &&
+           aligned16(a.C) && (a.batch == 1 || (a.sA % EPC == 0 && a.sB % EPC == 0 && a.sC % 8 == 0)) &&
+           (a.E == nullptr || (a.lde % 8 == 0 && aligned16(a.E) && (a.batch == 1 || a.sE % 8 == 0)));
+  };
+  int tm, tn;
+  const bool big = HALF && fast_for(256) && tiles_for(256, tm, tn) >= 512;
+  const int bm = big ? 256 : BM;
+  const long long grid = tiles_for(bm, tm, tn);
+  p.tiles_m = tm;
+  p.tiles_n = tn;
+  p.tiles_per_mat = OP == OP_GEMM ? tm * tn : tm * (tm + 1) / 2;
   if (grid <= 0 || grid > 0x7fffffffLL) return DION3_ERR_UNSUPPORTED;
 
-  const bool bt = OP == OP_GEMM;
-  bool fast = a.M % BM == 0 && a.N % BM == 0 && a.K % BKE == 0 &&
-              a.lda % EPC == 0 && a.ldb % EPC == 0 && aligned16(a.A) && aligned16(a.B) &&
-              (a.batch == 1 || (a.sA % EPC == 0 && a.sB % EPC == 0));
-  (void)bt;
   static const char* names[4] = {"syrk", "sym_sq_add", "sym_mul", "gemm_qx"};
   TimedLaunch tl(names[OP], s);
-  if (fast)
+  if (big) {
+    if constexpr (HALF)
+      hipLaunchKernelGGL((gemm256_kernel<T, TO, OP>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+  } else if (fast_for(BM))
     hipLaunchKernelGGL((gemm_kernel<T, TO, OP, false, BM>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
   else
     hipLaunchKernelGGL((gemm_kernel<T, TO, OP, true, BM>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);

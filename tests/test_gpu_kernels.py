@@ -266,3 +266,71 @@ def test_gemm_deterministic(d):
         torch.cuda.synchronize()
         outs.append(bits(C))
     assert np.array_equal(outs[0], outs[1])
+
+
+# ---------------------------------------------- large-tile launch configuration
+# Batched shapes of the Newton-Schulz products at the sizes the step uses
+# (k = 1024 and 1280 selected lines, m up to 11008), large enough that the
+# library takes its 256 x 256 tile.  Every matrix is checked for exact
+# symmetry; a sample of matrices is compared with fp64 products.  (The
+# library picks the large tile when a launch has at least 512 of them.)
+def _sample(b):
+    return sorted({0, b // 2, b - 1})
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("b,n,kd", [(52, 1024, 1024), (52, 1024, 11008), (36, 1280, 1280)])
+def test_syrk_large_tiles(d, dt, b, n, kd):
+    A = synth.dense(n, kd, b, dtype=dt, device=DEV, seed=n + kd + b)
+    C = torch.full((b, n, n), float("nan"), dtype=TD[dt], device=DEV)
+    d.dion3_syrk(A, C)
+    torch.cuda.synchronize()
+    cb = bits(C)
+    assert np.array_equal(cb, cb.transpose(0, 2, 1))
+    for i in _sample(b):
+        a = to64(A[i])
+        got = to64(C[i])
+        assert np.all(np.isfinite(got))
+        assert rel_fro(got, a @ a.T) <= TOL[dt], i
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("b,n", [(52, 1024), (36, 1280)])
+def test_sym_products_large_tiles(d, dt, b, n):
+    A = synth.symmetric(n, b, dtype=dt, device=DEV, seed=31)
+    B = synth.symmetric(n, b, dtype=dt, device=DEV, seed=32)
+    C = torch.empty_like(A)
+    al, be, ga = 2.0315, -4.7750, 3.4445
+    d.dion3_sym_sq_add(A, B, C, alpha=al, beta=be, gamma=ga)
+    torch.cuda.synchronize()
+    cb = bits(C)
+    assert np.array_equal(cb, cb.transpose(0, 2, 1))
+    for i in _sample(b):
+        a, bb = to64(A[i]), to64(B[i])
+        assert rel_fro(to64(C[i]), al * a @ a + be * bb + ga * np.eye(n)) <= TOL[dt], i
+    # product of two commuting polynomials of one symmetric matrix
+    S = A
+    P = torch.empty_like(A)
+    d.dion3_sym_sq_add(S, S, P, alpha=0.4, beta=-0.2, gamma=0.3)   # P = 0.4 S^2 - 0.2 S + 0.3 I
+    C2 = torch.empty_like(A)
+    d.dion3_sym_mul(S, P, C2, alpha=1.0)
+    torch.cuda.synchronize()
+    cb = bits(C2)
+    assert np.array_equal(cb, cb.transpose(0, 2, 1))
+    for i in _sample(b):
+        ref = to64(S[i]) @ to64(P[i])
+        ref = np.tril(ref) + np.tril(ref, -1).T
+        assert rel_fro(to64(C2[i]), ref) <= TOL[dt], i
+
+
+@pytest.mark.parametrize("dt,odt", [("f16", "f16"), ("bf16", "bf16"), ("f16", "f32")])
+@pytest.mark.parametrize("b,k,m", [(8, 1024, 4096), (3, 1024, 11008), (6, 1280, 5120)])
+def test_gemm_qx_large_tiles(d, dt, odt, b, k, m):
+    Q = synth.symmetric(k, b, dtype=dt, device=DEV, seed=k + b)
+    X = synth.dense(k, m, b, dtype=dt, device=DEV, seed=m + b)
+    Y = torch.empty(b, k, m, dtype=TD[odt], device=DEV)
+    d.dion3_gemm(Q, X, Y, alpha=1.0)
+    torch.cuda.synchronize()
+    for i in _sample(b):
+        ref = to64(Q[i]) @ to64(X[i])
+        assert rel_fro(to64(Y[i]), ref) <= TOL[odt if odt != "f32" else dt], i
