@@ -52,6 +52,33 @@ def parse():
     return ap.parse_args()
 
 
+# ------------------------------------------------------------------ traffic
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_7b_f025.txt")
+
+
+def measured_traffic(kernel: str, set_name: str, f: float):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary, or None if there is none for this workload or the
+    kernel's source has changed since the counters were taken."""
+    import hashlib
+    if set_name != "7b" or f != 0.25 or not os.path.exists(TRAFFIC_FILE):
+        return None
+    for line in open(TRAFFIC_FILE):
+        if not line.startswith("traffic "):
+            continue
+        kv = dict(tok.split("=", 1) for tok in line.split()[1:])
+        if kv.get("kernel") != kernel:
+            continue
+        h = hashlib.sha256()
+        for name in (kv["source"], "common.h"):
+            with open(os.path.join(ROOT, "muon_momentum_amd", "csrc", name), "rb") as fh:
+                h.update(fh.read())
+        if h.hexdigest()[:16] != kv["src_sha256"]:
+            return None
+        return float(kv["total_bytes"])
+    return None
+
+
 # ------------------------------------------------------------ work accounting
 def kernel_work(groups, ks, ns_bytes=2, store_bytes=2):
     """Algorithmic work per step of every kernel class of the library.
@@ -244,7 +271,8 @@ def main():
     t = table[dom]
     roof = {"kernel": dom, "bound": t["bound"], "achieved": t["achieved"],
             "peak": HBM_PEAK_GBS if t["bound"] == "hbm" else MFMA_F16_PEAK_TFLOPS,
-            "unit": t["unit"], "frac": t["frac"], "traffic": None,
+            "unit": t["unit"], "frac": t["frac"],
+            "traffic": measured_traffic(dom, args.set, args.f),
             "avg_launch_us": t["avg_launch_us"]}
 
     cpu = None
