@@ -1,4 +1,5 @@
-"""Shared helpers for the GPU parity tests (no method arithmetic here)."""
+"""Shared helpers for the GPU parity tests (no method arithmetic here: the
+step helper only calls the library's entry points)."""
 
 import numpy as np
 import torch
@@ -27,3 +28,43 @@ def bits(t: torch.Tensor) -> np.ndarray:
 def np_bits(x: np.ndarray, dtype: torch.dtype) -> np.ndarray:
     """Bit patterns of fp64 values that are exactly representable in dtype."""
     return bits(torch.from_numpy(np.asarray(x, dtype=np.float64)).to(dtype))
+
+
+def manual_step(d, groups, ks, params, eta, wd, mu, keep=None):
+    """The step through the individual entry points, batched like dion3_step
+    (groups of equal canonical (k, m) share one Newton-Schulz call).  Returns
+    per-group idx and the Newton-Schulz output O (canonical orientation) of
+    every matrix, or, with keep = {group: [matrix, ...]}, of those only."""
+    ns_t = d.torch_dtype(params.ns_dtype)
+    classes = {}
+    for gi, (W, M, G) in enumerate(groups):
+        n, m, ax = d.dion3_canonical(d.make_group(M))
+        classes.setdefault((ks[gi], m), []).append(gi)
+    idxs, Os = [None] * len(groups), [None] * len(groups)
+    for (k, m), members in classes.items():
+        nb = sum(groups[g][0].shape[0] for g in members)
+        X = torch.empty(nb, k, m, dtype=ns_t, device="cuda")
+        Ob = torch.empty_like(X)
+        off = 0
+        for g in members:
+            W, M, G = groups[g]
+            b = M.shape[0]
+            idx = torch.empty(b, k, dtype=torch.int32, device="cuda")
+            sqn = torch.empty(b, dtype=torch.float64, device="cuda")
+            d.dion3_momentum_rowsel(M, G, k, idx, None, sqn)
+            d.dion3_gather_rows(M, idx, k, sqn, X[off:off + b], eps=params.eps)
+            idxs[g] = idx
+            off += b
+        d.dion3_gram_ns(X, Ob, params)
+        off = 0
+        for g in members:
+            W, M, G = groups[g]
+            b = M.shape[0]
+            d.dion3_apply_rows(W, M, idxs[g], k, Ob[off:off + b], eta, wd, mu)
+            if keep is None:
+                Os[g] = Ob[off:off + b].clone()
+            else:
+                Os[g] = {j: Ob[off + j].clone() for j in keep.get(g, [])}
+            off += b
+    torch.cuda.synchronize()
+    return idxs, Os

@@ -1,0 +1,126 @@
+"""Parity at the full sizes of the transformer shape sets, in the launch
+configuration the benchmark times (same groups, same batched Newton-Schulz
+classes, same kernels and grids).
+
+The oracle runs the whole step on sampled matrices of every group: selected
+indices and M bit for bit, the W update bit for bit given the GPU's
+Newton-Schulz output O, and O within the fp16 tolerance (3e-2 relative
+Frobenius).  On the first step every eighth matrix of every group is also
+checked for a property that holds at any size: the selected lines are those
+of largest l1 norm (ties to the lower index), norms recomputed on the host
+from the step's input momentum (M0 = 0, so that momentum is G)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from helpers import bits, manual_step, np_bits, rel_fro, to64
+from muon_momentum_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def d():
+    import muon_momentum_amd.dion3 as mod
+    return mod
+
+
+def check_selection_property(Mc, idx, k):
+    """idx (ascending) holds the k lines of largest l1 norm, ties to lower index."""
+    keys = np.abs(Mc).sum(axis=1)
+    n = keys.shape[0]
+    assert idx.shape == (k,) and np.all(np.diff(idx) > 0) and idx[0] >= 0 and idx[-1] < n
+    if k == n:
+        return
+    sel = np.zeros(n, dtype=bool)
+    sel[idx] = True
+    lo, hi = keys[sel].min(), keys[~sel].max()
+    assert lo >= hi
+    if lo == hi:   # a tie at the boundary: tied unselected lines come after the tied selected ones
+        assert np.where(~sel & (keys == hi))[0].min() > np.where(sel & (keys == lo))[0].max()
+
+
+def run_set(d, name, f, steps, sample, prop_every=8):
+    groups = synth.shape_groups(name)
+    tensors = []
+    for gi, (r, c, b) in enumerate(groups):
+        W = synth.weights(r, c, b, dtype="bf16", device=DEV, group_seed=gi)
+        G = synth.gradient(r, c, b, dtype="bf16", device=DEV, group_seed=gi, step=0)
+        M = torch.zeros(b, r, c, dtype=torch.bfloat16, device=DEV)
+        tensors.append([W, M, G])
+    ks = [d.dion3_k_from_fraction(min(r, c), f) for r, c, _ in groups]
+    eta, mu = 0.02 / math.sqrt(f), 0.95
+    params = d.make_ns_params(ns_dtype=d.F16)
+    # the oracle's state of every sampled matrix (W, M), followed across steps
+    state = {(gi, j): [to64(tensors[gi][0][j]), np.zeros(groups[gi][:2])]
+             for gi, js in sample.items() for j in js}
+    worst = 0.0
+    for step in range(steps):
+        if step > 0:
+            for gi, (r, c, b) in enumerate(groups):
+                tensors[gi][2] = synth.gradient(r, c, b, dtype="bf16", device=DEV, group_seed=gi, step=step)
+        Gh = {key: to64(tensors[key[0]][2][key[1]]) for key in state}
+        Wpre = {key: to64(tensors[key[0]][0][key[1]]) for key in state}
+        idxs, Os = manual_step(d, [tuple(t) for t in tensors], ks, params, eta, 0.0, mu, keep=sample)
+        for gi, (r, c, b) in enumerate(groups):
+            ax = 0 if r <= c else 1
+            idx_all = idxs[gi].cpu().numpy()
+            if step == 0:
+                for j in range(0, b, prop_every):
+                    Gc = to64(tensors[gi][2][j])
+                    check_selection_property(Gc if ax == 0 else Gc.T, idx_all[j], ks[gi])
+            for j in sample.get(gi, []):
+                Wh, Mh = state[(gi, j)]
+                out = O.dion3_step(Wh, Mh, Gh[(gi, j)], k=ks[gi], mu=mu, eta=eta, fmt="bf16")
+                where = (name, f, step, gi, j)
+                assert np.array_equal(idx_all[j], out["idx"]), where
+                assert np.array_equal(bits(tensors[gi][1][j]), np_bits(out["M"], torch.bfloat16)), where
+                Og = to64(Os[gi][j])
+                err = rel_fro(Og, out["O"])
+                worst = max(worst, err)
+                assert err <= 3e-2, (where, err)
+                Mc = O.momentum_accumulate(Mh, Gh[(gi, j)], "bf16")
+                Wc, Mcc = (Wpre[(gi, j)], Mc) if ax == 0 else (Wpre[(gi, j)].T, Mc.T)
+                Wg, _ = O.apply_rows(Wc, Mcc, out["idx"], Og, eta, 0.0, mu, "bf16")
+                if ax == 1:
+                    Wg = Wg.T
+                assert np.array_equal(bits(tensors[gi][0][j]), np_bits(Wg, torch.bfloat16)), where
+                state[(gi, j)] = [out["W"], out["M"]]
+        del Os
+    del tensors
+    torch.cuda.empty_cache()
+    return worst
+
+
+def test_7b_quarter(d):
+    """The benchmarked workload: 7B shape set, f = 1/4, two matrices per group."""
+    groups = synth.shape_groups("7b")
+    worst = run_set(d, "7b", 0.25, 1, {gi: [0, b - 1] for gi, (_, _, b) in enumerate(groups)})
+    print(f"7b f=1/4 worst O error {worst:.2e}")
+
+
+def test_1b_eighth(d):
+    groups = synth.shape_groups("1b")
+    worst = run_set(d, "1b", 0.125, 1, {gi: [0, b - 1] for gi, (_, _, b) in enumerate(groups)})
+    print(f"1b f=1/8 worst O error {worst:.2e}")
+
+
+@pytest.mark.parametrize("f", [0.5, 1.0])
+def test_7b_half_and_full(d, f):
+    """f = 1/2 and f = 1 (plain Muon through Gram Newton-Schulz); the oracle
+    follows one attention matrix, the property check covers every group."""
+    worst = run_set(d, "7b", f, 1, {0: [0]})
+    print(f"7b f={f} worst O error {worst:.2e}")
+
+
+def test_14b_three_steps(d):
+    """Three consecutive steps: the error-feedback momentum carries across and
+    stays bit-exact; one square and one column-selected matrix followed."""
+    groups = synth.shape_groups("14b")
+    worst = run_set(d, "14b", 0.25, 3, {0: [0], 2: [groups[2][2] - 1]})
+    print(f"14b f=1/4 three steps worst O error {worst:.2e}")

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle as O
-from helpers import bits, np_bits, rel_fro, to64
+from helpers import bits, manual_step, np_bits, rel_fro, to64
 from muon_momentum_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -22,41 +22,6 @@ TD = {"bf16": torch.bfloat16, "f32": torch.float32, "f16": torch.float16}
 def d():
     import muon_momentum_amd.dion3 as mod
     return mod
-
-
-def manual_step(d, groups, ks, params, eta, wd, mu):
-    """The step through the individual entry points; returns per-group idx and
-    the Newton-Schulz output O of every matrix (canonical orientation)."""
-    ns_t = d.torch_dtype(params.ns_dtype)
-    classes = {}
-    for gi, (W, M, G) in enumerate(groups):
-        n, m, ax = d.dion3_canonical(d.make_group(M))
-        classes.setdefault((ks[gi], m), []).append(gi)
-    idxs, Os = [None] * len(groups), [None] * len(groups)
-    for (k, m), members in classes.items():
-        nb = sum(groups[g][0].shape[0] for g in members)
-        X = torch.empty(nb, k, m, dtype=ns_t, device=DEV)
-        Ob = torch.empty_like(X)
-        off = 0
-        for g in members:
-            W, M, G = groups[g]
-            b = M.shape[0]
-            idx = torch.empty(b, k, dtype=torch.int32, device=DEV)
-            sqn = torch.empty(b, dtype=torch.float64, device=DEV)
-            d.dion3_momentum_rowsel(M, G, k, idx, None, sqn)
-            d.dion3_gather_rows(M, idx, k, sqn, X[off:off + b], eps=params.eps)
-            idxs[g] = idx
-            off += b
-        d.dion3_gram_ns(X, Ob, params)
-        off = 0
-        for g in members:
-            W, M, G = groups[g]
-            b = M.shape[0]
-            d.dion3_apply_rows(W, M, idxs[g], k, Ob[off:off + b], eta, wd, mu)
-            Os[g] = Ob[off:off + b].clone()
-            off += b
-    torch.cuda.synchronize()
-    return idxs, Os
 
 
 def test_config1_fp32_f1_three_steps(d):
