@@ -23,12 +23,13 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
 
-// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.  Written as a
+// select so that it does not branch inside a wave.
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t quiet = (u >> 16) | 0x40u;
+  return (bf16_t)(((u & 0x7fffffffu) > 0x7f800000u) ? quiet : rounded);
 }
 
 // fp64 -> bf16 with a single round-to-nearest-even of the fp64 value.

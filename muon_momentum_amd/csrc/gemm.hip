@@ -53,6 +53,10 @@ template <> struct Mma<float> {
 };
 
 constexpr int kThreads = 256;
+#ifndef DION3_STAGES
+#define DION3_STAGES 5
+#endif
+constexpr int kStages = DION3_STAGES;   // LDS stages of the large-tile kernel
 constexpr int kRowBytes = 128;          // bytes of K per LDS row per stage
 constexpr int kChunks = kRowBytes / 16; // 8 chunks per row
 
@@ -341,19 +345,50 @@ __device__ __forceinline__ void lds_dma16(const int4v& rsrc, const void* lds, in
                :: "s"(m0), "v"(voffset), "s"(rsrc), "s"(soffset) : "memory", "m0");
 }
 
-template <typename T, typename TO, int OP>
+// LDS position of 16-byte chunk `chunk` of row `row` of a K-contiguous operand
+// stage (32 K elements = 64 bytes per row).  The 16 lanes of an LDS read phase
+// read one chunk column of 16 consecutive rows: 4 rows share each 256-byte
+// line and (row / 4) mod 4 permutes the chunk within its 64 bytes.
+__device__ __forceinline__ int swz32(int row, int chunk) {
+  return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
+}
+
+// Byte offset of element column n (a multiple of 4) of row kr in an
+// N-contiguous stage (32 rows of 256 elements, 512 bytes): 16-byte chunk n/8
+// sits at chunk (n/8) xor 2 (kr mod 4), so the four rows read by one
+// transposing LDS read phase fall in distinct 32-byte slots.
+__device__ __forceinline__ int swzn(int kr, int n) {
+  return kr * 512 + ((((n >> 3) ^ (2 * (kr & 3)))) << 4) + ((n & 4) << 1);
+}
+
+__device__ __forceinline__ void wait_vm_stages(int n) {   // n: DMA stages allowed in flight
+  if (n <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if (n == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if (n == 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+}
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+
+// Large-tile kernel (fp16 / bf16, whole tiles only).  Stage s of the K loop
+// (32 K elements of both operands, 32 KB) lives in LDS buffer s mod NBUF.  Its
+// loads are issued right after the barrier that ends stage s - NBUF (the last
+// use of that buffer) and must have landed by the barrier that ends stage
+// s - 2; the first k-step's fragments of stage s are then read during stage
+// s - 1, so a wave leaves every barrier with its next MFMA operands in
+// registers.  Each wave issues 8 one-kilobyte DMA instructions per stage.
+template <typename T, typename TO, int OP, int NBUF>
 __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm256_kernel(KParams p) {
   constexpr bool SYM = OP != OP_GEMM;
   constexpr bool BT = OP == OP_GEMM;
   constexpr int BM = 256, BN = 256;
-  constexpr int BKE = kRowBytes / 2;          // 64 K elements per stage
+  constexpr int BK = 32;                      // K elements per stage
   constexpr int WT = 128;                     // wave tile edge
   constexpr int SUB = WT / 32;                // 4 x 4 MFMA tiles per wave
-  constexpr int ROWS_PER_INSTR = 8;           // 1 KB = 8 LDS rows per wave instruction
-  constexpr int INSTR = BM / (4 * ROWS_PER_INSTR);   // 8 instructions per wave per operand
+  constexpr int STAGE = 32768;                // bytes per stage (both operands)
 
-  __shared__ __attribute__((aligned(1024))) char smem[2][2][BM * kRowBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * STAGE];
 
   const int G = gridDim.x;
   const int wg = blockIdx.x;
@@ -383,23 +418,69 @@ void gemm256_kernel(KParams p) {
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // direct-to-LDS addressing: this lane fetches row (wave*8 + lane/8) + 32 s of
-  // the tile, chunk (lane%8) ^ (lane/8); byte offsets relative to the tile origin
+  // ---- DMA addressing.  K-contiguous operand: wave instruction s (0..3)
+  // covers tile rows 64 s + 16 wave + [0, 16); lane L fetches row
+  // 64 s + 16 wave + L/4 and the chunk whose swizzled position is L mod 4.
   const int4v ra = make_rsrc(A, (long long)p.M * p.lda * 2);
-  const int lrow = wave * ROWS_PER_INSTR + (lane >> 3);
-  const int lchunk = (lane & 7) ^ ((lrow >> 1) & 7);   // rows r0 + 32 s keep (row/2) mod 8
-  const int va = ((m0 + lrow) * (int)p.lda + lchunk * 8) * 2;
-  const int rstep_a = 4 * ROWS_PER_INSTR * (int)p.lda * 2;   // 32 rows
+  const int va = ((m0 + 16 * wave + (lane >> 2)) * (int)p.lda + (((lane & 3) ^ (lane >> 4)) << 3)) * 2;
+  const int ka = 64 * (int)p.lda * 2;                 // +64 rows per instruction
+  // B operand: K-contiguous (symmetric products) like A, or N-contiguous (Q X):
+  // instruction s covers stage rows 8 s + 2 wave + {0, 1}; lane L fetches
+  // row 8 s + 2 wave + L/32, the chunk whose swizzled position is L mod 32
   const int4v rb = make_rsrc(B, BT ? (long long)p.K * p.ldb * 2 : (long long)p.N * p.ldb * 2);
-  const int vb = ((n0 + lrow) * (int)p.ldb + lchunk * 8) * 2;
-  const int rstep_b = 4 * ROWS_PER_INSTR * (int)p.ldb * 2;
-  // Q X: the N-contiguous B operand is read with ordinary buffer loads into
-  // registers (the compiler tracks them); this lane's 8 x 8 block starts at
-  // row 8 kb, column n0 + 8 nb of the stage
-  const __amdgpu_buffer_rsrc_t rbq = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<T*>(B), 0, (int)(BT ? min((long long)p.K * p.ldb * 2, 0x7fffffffLL) : 0), 0x00020000);
-  const int vbt = ((tid & 7) * 8 * (int)p.ldb + n0 + (tid >> 3) * 8) * 2;
-  (void)rb; (void)vb; (void)rstep_b; (void)rbq; (void)vbt;
+  int vb, kb;
+  if (!BT) {
+    vb = ((n0 + 16 * wave + (lane >> 2)) * (int)p.ldb + (((lane & 3) ^ (lane >> 4)) << 3)) * 2;
+    kb = 64 * (int)p.ldb * 2;
+  } else {
+    const int kr = 2 * wave + (lane >> 5);
+    vb = (kr * (int)p.ldb + n0 + (((lane & 31) ^ (2 * (kr & 3))) << 3)) * 2;
+    kb = 8 * (int)p.ldb * 2;                          // +8 rows per instruction
+  }
+
+  // one DMA instruction x (0..3: operand A, 4..7: operand B) of stage s
+  auto dma = [&](int s, int x) {
+    char* buf = smem + (s % NBUF) * STAGE;
+    const int k0 = s * BK;
+    const int q = x & 3;
+    if (x < 4) {
+      lds_dma16(ra, buf + (64 * q + 16 * wave) * 64, va, k0 * 2 + q * ka);
+    } else if (!BT) {
+      lds_dma16(rb, buf + 16384 + (64 * q + 16 * wave) * 64, vb, k0 * 2 + q * kb);
+    } else {
+      lds_dma16(rb, buf + 16384 + (8 * q + 2 * wave) * 512, vb, k0 * (int)p.ldb * 2 + q * kb);
+    }
+  };
+  auto issue_stage = [&](int s) {
+#pragma unroll
+    for (int x = 0; x < 8; ++x) dma(s, x);
+  };
+
+  // fragments of one k-step (16 K elements): A rows wm*128 + 32 i + lane%32;
+  // B either likewise (K-contiguous) or through transposing reads (Q X)
+  auto read_a = [&](uint4& f, int s, int st, int i) {
+    const char* buf = smem + (s % NBUF) * STAGE;
+    f = *(const uint4*)(buf + swz32(wm * WT + i * 32 + (lane & 31), 2 * st + (lane >> 5)));
+  };
+  auto read_b = [&](uint4& f, int s, int st, int j) {
+    const char* buf = smem + (s % NBUF) * STAGE + 16384;
+    if (!BT) {
+      f = *(const uint4*)(buf + swz32(wn * WT + j * 32 + (lane & 31), 2 * st + (lane >> 5)));
+    } else {
+      // lane = 16 g + 4 q + t addresses row 16 st + 8 (g/2) + 4 h + q and
+      // columns 16 (g mod 2) + 4 t .. +3 of the fragment's 32; the transposing
+      // read hands each lane its column's four consecutive K values
+      const int g = lane >> 4, q = (lane >> 2) & 3, tt = lane & 3;
+      const int n = wn * WT + j * 32 + 16 * (g & 1) + 4 * tt;
+      const int kr0 = 16 * st + 8 * (g >> 1) + q;
+      const short4v h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) short4v*)(__attribute__((address_space(3))) char*)(buf + swzn(kr0, n)));
+      const short4v h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) short4v*)(__attribute__((address_space(3))) char*)(buf + swzn(kr0 + 4, n)));
+      f = make_uint4(__builtin_bit_cast(uint2, h0).x, __builtin_bit_cast(uint2, h0).y,
+                     __builtin_bit_cast(uint2, h1).x, __builtin_bit_cast(uint2, h1).y);
+    }
+  };
 
   floatx16 acc[SUB][SUB];
 #pragma unroll
@@ -409,85 +490,61 @@ void gemm256_kernel(KParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  uint4 rbt[8];   // transposed-B staging (Q X only)
+  const int KT = p.K / BK;
+  const int pre = KT < NBUF - 1 ? KT : NBUF - 1;
+  for (int s = 0; s < pre; ++s) issue_stage(s);
+  wait_vm_stages(pre - (KT < 2 ? KT : 2));            // stages 0 and 1 landed
+  __syncthreads();
 
-  auto issue_stage = [&](int buf, int k0) {
-    char* sa = smem[buf][0] + wave * ROWS_PER_INSTR * kRowBytes;
+  uint4 fa0[SUB], fb0[SUB], fa1[SUB], fb1[SUB];
 #pragma unroll
-    for (int s = 0; s < INSTR; ++s) lds_dma16(ra, sa + s * 4 * ROWS_PER_INSTR * kRowBytes, va, k0 * 2 + s * rstep_a);
-    if (!BT) {
-      char* sb = smem[buf][1] + wave * ROWS_PER_INSTR * kRowBytes;
-#pragma unroll
-      for (int s = 0; s < INSTR; ++s) lds_dma16(rb, sb + s * 4 * ROWS_PER_INSTR * kRowBytes, vb, k0 * 2 + s * rstep_b);
-    } else {
-      // an 8 (K) x 8 (N) block per thread (kb = tid mod 8, nb = tid / 8): rows
-      // k0 + 8 kb + r, columns n0 + 8 nb + c; eight consecutive lanes share
-      // nb, so each LDS write instruction fills whole 128-byte rows
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rbq, vbt, (k0 + r) * (int)p.ldb * 2, 0);
-        rbt[r] = make_uint4(v[0], v[1], v[2], v[3]);
-      }
-    }
-  };
-  auto finish_stage = [&](int buf) {
-    if (BT) {
-      char* sb = smem[buf][1];
-      const int kb = tid & 7, nb = tid >> 3;
-      uint4 tr[8];
-      transpose8x8<T>(rbt, tr);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) *(uint4*)(sb + swz(nb * 8 + c, kb)) = tr[c];
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  };
+  for (int i = 0; i < SUB; ++i) { read_a(fa0[i], 0, 0, i); read_b(fb0[i], 0, 0, i); }
 
-  const int KT = p.K / BKE;
-  issue_stage(0, 0);
-  finish_stage(0);
-
+  // One stage = 2 k-steps x 4 groups of 4 MFMAs.  Group x of a step first
+  // issues one DMA instruction of the stage NBUF - 1 ahead (spread out so
+  // the vector memory queue never stalls the wave), then reads two fragments
+  // of the next k-step (B fragments first), then runs its 4 MFMAs.
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) issue_stage(cur ^ 1, (kt + 1) * BKE);
-    const char* sa = smem[cur][0];
-    const char* sb = smem[cur][1];
-    // every fragment of the stage gets its own registers (32 x 16 bytes per
-    // lane), so reads for the next k-step can be in flight during this one
-    constexpr int STEPS = kChunks / 2;
-    uint4 fa[STEPS][SUB], fb[STEPS][SUB];
-    static_for<STEPS>([&](auto sc) {
-      constexpr int st = decltype(sc)::value;
-      const int chunk = 2 * st + (lane >> 5);
+    const bool iss = kt + NBUF - 1 < KT;
+    static_for<2 * SUB>([&](auto gxc) {
+      constexpr int gx = decltype(gxc)::value;
+      constexpr int st = gx / SUB, x = gx % SUB;     // k-step, MFMA row block
+      __builtin_amdgcn_sched_barrier(0);
+      if (iss) dma(kt + NBUF - 1, gx);
+      // next k-step: step 1 of this stage, or step 0 of the next stage
+      const int ns = st == 0 ? kt : kt + 1;
+      const int nst = st == 0 ? 1 : 0;
+      uint4 (&na)[SUB] = st == 0 ? fa1 : fa0;
+      uint4 (&nb)[SUB] = st == 0 ? fb1 : fb0;
+      if (x < 2) {
+        read_b(nb[2 * x], ns, nst, 2 * x);
+        read_b(nb[2 * x + 1], ns, nst, 2 * x + 1);
+      } else {
+        read_a(na[2 * x - 4], ns, nst, 2 * x - 4);
+        read_a(na[2 * x - 3], ns, nst, 2 * x - 3);
+      }
+      uint4 (&ca)[SUB] = st == 0 ? fa0 : fa1;
+      uint4 (&cbv)[SUB] = st == 0 ? fb0 : fb1;
 #pragma unroll
-      for (int i = 0; i < SUB; ++i) fa[st][i] = *(const uint4*)(sa + swz(wm * WT + i * 32 + (lane & 31), chunk));
-#pragma unroll
-      for (int j = 0; j < SUB; ++j) fb[st][j] = *(const uint4*)(sb + swz(wn * WT + j * 32 + (lane & 31), chunk));
+      for (int j = 0; j < SUB; ++j) Mma<T>::run(acc[x][j], ca[x], cbv[j]);
     });
-    static_for<STEPS>([&](auto sc) {
-      constexpr int st = decltype(sc)::value;
-#pragma unroll
-      for (int i = 0; i < SUB; ++i)
-#pragma unroll
-        for (int j = 0; j < SUB; ++j) Mma<T>::run(acc[i][j], fa[st][i], fb[st][j]);
-    });
-    // schedule: step 0's reads, then each step's MFMAs with the next step's
-    // reads interleaved (one read per two MFMAs)
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * SUB, 0);
-    static_for<(STEPS - 1) * 2 * SUB>([&](auto) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    });
-    __builtin_amdgcn_sched_group_barrier(0x008, SUB * SUB, 0);
-    if (kt + 1 < KT) finish_stage(cur ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < KT) {
+      // stage kt + 2 must land before this barrier; later stages may fly on
+      const int last_issued = kt + NBUF - 1 < KT ? kt + NBUF - 1 : KT - 1;
+      wait_vm_stages(kt + 2 < KT ? last_issued - (kt + 2) : 0);
+      __syncthreads();
+    }
   }
 
-  // ---- epilogue: the lower triangle and its mirror; diagonal tiles write
-  // every entry exactly once (i >= j directly, i > j mirrored)
+  // ---- epilogue.  Direct tile: each lane stores its values at C[gi][gj].
+  // Mirror (symmetric ops): the values are also written transposed into LDS,
+  // then copied out as whole 512-byte rows to C[gj][gi]; on diagonal tiles
+  // only the strict upper part is copied, so every entry is written once.
   TO* C = (TO*)p.C + bu * p.sC;
   const TO* E = (const TO*)p.E + (p.E ? bu * p.sE : 0);
   const bool diag_tile = SYM && ti == tj;
-  if (diag_tile && wm < wn) return;            // the upper quadrant mirrors the lower one
+  const bool upper_wave = diag_tile && wm < wn;   // the mirror of the lower quadrant
   constexpr bool HAS_E = OP == OP_SQ_ADD || OP == OP_SYRK;
   const bool use_e = OP == OP_SQ_ADD || (OP == OP_SYRK && p.beta != 0.f);
   // The epilogue operand is symmetric, so the four values E[gi..gi+3][gj] this
@@ -495,7 +552,7 @@ void gemm256_kernel(KParams p) {
   // issued before any store (the memory counter also counts stores).
   uint2 epk[SUB][SUB][4];
   if constexpr (HAS_E) {
-    if (use_e) {
+    if (use_e && !upper_wave) {
       static_for<SUB>([&](auto ic) {
         static_for<SUB>([&](auto jc) {
           constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
@@ -512,48 +569,89 @@ void gemm256_kernel(KParams p) {
       });
     }
   }
+  // transposed tile in LDS: row c = gj - n0 (256 rows of 512 bytes), 8-byte
+  // granule r/4 of r = gi - m0 at position (r/4) xor (c mod 32)
+  char* tl = smem;
+  if (SYM) __syncthreads();                      // the last stage's LDS reads are done
   asm volatile("" ::: "memory");
-  static_for<SUB>([&](auto ic) {
-    static_for<SUB>([&](auto jc) {
-      constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
-      const int gi0 = m0 + wm * WT + i * 32;
-      const int gj0 = n0 + wn * WT + j * 32;
-      if (SYM && gi0 < gj0) return;            // above the diagonal (diagonal tiles only)
-      const bool below = !SYM || gi0 > gj0;    // whole 32 x 32 block strictly below
-      const int gj = gj0 + (lane & 31);
-      static_for<4>([&](auto gc) {
-        constexpr int g = decltype(gc)::value;
-        const int gib = gi0 + 8 * g + 4 * (lane >> 5);
-        union { uint2 u; TO e[4]; } ev;
-        if constexpr (HAS_E) ev.u = epk[i][j][g];
-        TO vv[4];
-        static_for<4>([&](auto qc) {
-          constexpr int q = decltype(qc)::value;
-          const int gi = gib + q;
-          float v = p.alpha * acc[i][j][4 * g + q];
-          if constexpr (HAS_E) {
-            if (use_e) v += p.beta * Store<TO>::to_f32(ev.e[q]);
+  // per-lane bases: element (32 i + 8 g + q, 32 j) of this wave's quadrant
+  const int lc = lane & 31, lh = lane >> 5;
+  TO* cb = C + (long long)(m0 + wm * WT + 4 * lh) * p.ldc + (n0 + wn * WT + lc);
+  char* tb = tl + (wn * WT + lc) * 512;
+  if (!upper_wave) {
+    static_for<SUB>([&](auto ic) {
+      static_for<SUB>([&](auto jc) {
+        constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
+        const int gi0 = m0 + wm * WT + i * 32;
+        const int gj0 = n0 + wn * WT + j * 32;
+        if (SYM && gi0 < gj0) return;            // above the diagonal (diagonal tiles only)
+        const bool dblk = SYM && gi0 == gj0;     // a 32 x 32 block on the diagonal
+        static_for<4>([&](auto gc) {
+          constexpr int g = decltype(gc)::value;
+          uint32_t ebits[2] = {0u, 0u};
+          if constexpr (HAS_E && sizeof(TO) == 2) { ebits[0] = epk[i][j][g].x; ebits[1] = epk[i][j][g].y; }
+          float v[4];
+          static_for<4>([&](auto qc) {
+            constexpr int q = decltype(qc)::value;
+            v[q] = p.alpha * acc[i][j][4 * g + q];
+            if constexpr (HAS_E && sizeof(TO) == 2) {
+              if (use_e) {
+                const uint16_t eb = (uint16_t)(ebits[q >> 1] >> (16 * (q & 1)));
+                v[q] += p.beta * Store<TO>::to_f32(__builtin_bit_cast(TO, eb));
+              }
+            }
+          });
+          if (OP == OP_SQ_ADD && dblk) {
+            // gi == gj: row 8 g + 4 lh + q of the block equals column lc
+            static_for<4>([&](auto qc) {
+              constexpr int q = decltype(qc)::value;
+              if (8 * g + 4 * lh + q == lc) v[q] += p.gamma;
+            });
           }
-          if (OP == OP_SQ_ADD && gi == gj) v += p.gamma;
-          vv[q] = Store<TO>::from_f32(v);
-          if (below || gi >= gj) C[(long long)gi * p.ldc + gj] = vv[q];
-        });
-        if (SYM) {
-          if (below) {
-            // C[gj][gib .. gib+3]: four consecutive elements, one 8-byte store
-            union { uint2 u; TO e[4]; } pk;
-            static_for<4>([&](auto qc) { pk.e[decltype(qc)::value] = vv[decltype(qc)::value]; });
-            *(uint2*)(C + (long long)gj * p.ldc + gib) = pk.u;
+          TO o[4];
+          static_for<4>([&](auto qc) { o[decltype(qc)::value] = Store<TO>::from_f32(v[decltype(qc)::value]); });
+          TO* dst = cb + (long long)(32 * i + 8 * g) * p.ldc + 32 * j;
+          if (!dblk) {
+            static_for<4>([&](auto qc) { dst[(long long)decltype(qc)::value * p.ldc] = o[decltype(qc)::value]; });
           } else {
             static_for<4>([&](auto qc) {
               constexpr int q = decltype(qc)::value;
-              if (gib + q > gj) C[(long long)gj * p.ldc + gib + q] = vv[q];
+              if (8 * g + 4 * lh + q >= lc) dst[(long long)q * p.ldc] = o[q];
             });
           }
-        }
+          if constexpr (SYM && sizeof(TO) == 2) {
+            const uint2 pk = make_uint2(
+                (uint32_t)__builtin_bit_cast(uint16_t, o[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, o[1]) << 16),
+                (uint32_t)__builtin_bit_cast(uint16_t, o[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, o[3]) << 16));
+            const int r4 = wm * 32 + i * 8 + 2 * g + lh;     // (gi - m0) / 4
+            *(uint2*)(tb + j * 32 * 512 + ((r4 ^ lc) << 3)) = pk;
+          }
+        });
       });
     });
-  });
+  }
+  if constexpr (SYM) {
+    __syncthreads();
+    // copy: thread t takes 16-byte chunk u = t mod 32 of rows t/32 + 8 s
+    const int u = tid & 31;
+#pragma unroll 4
+    for (int s = 0; s < 32; ++s) {
+      const int c = (tid >> 5) + 8 * s;
+      const int x = c & 31;
+      uint4 v = *(const uint4*)(tl + c * 512 + ((u ^ (x >> 1)) << 4));
+      if (x & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+      TO* dst = C + (long long)(n0 + c) * p.ldc + m0 + 8 * u;
+      if (!diag_tile || 8 * u > c) {
+        *(uint4*)dst = v;
+      } else if (8 * u + 7 > c) {
+        union { uint4 v; TO e[8]; } w;
+        w.v = v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (8 * u + e > c) dst[e] = w.e[e];
+      }
+    }
+  }
 }
 
 template <typename T, typename TO, int OP, int BM>
@@ -584,7 +682,10 @@ static int launch_typed(const GemmArgs& a, hipStream_t s) {
            (a.E == nullptr || (a.lde % 8 == 0 && aligned16(a.E) && (a.batch == 1 || a.sE % 8 == 0)));
   };
   int tm, tn;
-  const bool big = HALF && fast_for(256) && tiles_for(256, tm, tn) >= 512;
+  // the large-tile kernel addresses each operand with 32-bit byte offsets
+  const bool fits32 = (long long)a.M * a.lda * 2 < (1LL << 31) &&
+                      (long long)(OP == OP_GEMM ? a.K : a.N) * a.ldb * 2 < (1LL << 31);
+  const bool big = HALF && fits32 && fast_for(256) && tiles_for(256, tm, tn) >= 512;
   const int bm = big ? 256 : BM;
   const long long grid = tiles_for(bm, tm, tn);
   p.tiles_m = tm;
@@ -596,7 +697,7 @@ static int launch_typed(const GemmArgs& a, hipStream_t s) {
   TimedLaunch tl(names[OP], s);
   if (big) {
     if constexpr (HALF)
-      hipLaunchKernelGGL((gemm256_kernel<T, TO, OP>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL((gemm256_kernel<T, TO, OP, kStages>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
   } else if (fast_for(BM))
     hipLaunchKernelGGL((gemm_kernel<T, TO, OP, false, BM>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
   else
@@ -609,7 +710,8 @@ static int dispatch(const GemmArgs& a, hipStream_t s) {
   constexpr int BM = 128;
   if (a.dtype == DION3_F16) {
     if (a.out_dtype == DION3_F16) return launch_typed<f16, f16, OP, BM>(a, s);
-    if (a.out_dtype == DION3_F32 && OP == OP_GEMM) return launch_typed<f16, float, OP, BM>(a, s);
+    if constexpr (OP == OP_GEMM)
+      if (a.out_dtype == DION3_F32) return launch_typed<f16, float, OP, BM>(a, s);
   } else if (a.dtype == DION3_BF16) {
     if (a.out_dtype == DION3_BF16) return launch_typed<bf16_t, bf16_t, OP, BM>(a, s);
   } else if (a.dtype == DION3_F32) {

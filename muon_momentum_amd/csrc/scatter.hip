@@ -67,13 +67,22 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(
   const TS* src = M + b * bstride + (long long)r * cols;
   TX* dst = X + ((long long)b * k + i) * cols;
   if (VEC) {
-    for (int c = lane * 8; c < cols; c += 64 * 8) {
-      typename Pack8<TS>::U a;
-      typename Pack8<TX>::U o;
-      load8<TS>(a, src + c);
+    // U chunks of 512 elements per wave in flight: all loads first, then stores
+    constexpr int U = 4;
+    for (int c0 = lane * 8; c0 < cols; c0 += 64 * 8 * U) {
+      typename Pack8<TS>::U a[U];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o.e[e] = Store<TX>::from_f32(Store<TS>::to_f32(a.e[e]) * sc);
-      store8<TX>(dst + c, o);
+      for (int u = 0; u < U; ++u)
+        if (c0 + u * 512 < cols) load8<TS>(a[u], src + c0 + u * 512);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (c0 + u * 512 < cols) {
+          typename Pack8<TX>::U o;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o.e[e] = Store<TX>::from_f32(Store<TS>::to_f32(a[u].e[e]) * sc);
+          store8<TX>(dst + c0 + u * 512, o);
+        }
+      }
     }
   } else {
     for (int c = lane; c < cols; c += 64)
@@ -118,7 +127,7 @@ template <typename TS, typename TO, bool VEC>
 __global__ __launch_bounds__(256) void apply_rows_kernel(
     TS* __restrict__ W, TS* __restrict__ M, long long bstride, int nlines, int cols,
     const int32_t* __restrict__ idx, int k, const TO* __restrict__ O, long long ostride, float eta,
-    float u, int decay, float mu) {
+    float u_, int decay, float mu) {
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = blockIdx.x * 4 + wave;
@@ -129,23 +138,37 @@ __global__ __launch_bounds__(256) void apply_rows_kernel(
   TS* mm = M + b * bstride + (long long)r * cols;
   const TO* o = O + b * ostride + (long long)i * cols;
   if (VEC) {
-    for (int c = lane * 8; c < cols; c += 64 * 8) {
-      typename Pack8<TS>::U vw, vm;
-      typename Pack8<TO>::U vo;
-      load8<TS>(vw, w + c);
-      load8<TS>(vm, mm + c);
-      load8<TO>(vo, o + c);
+    // U chunks of 512 elements per wave in flight: all loads first, then stores
+    constexpr int U = 4;
+    for (int c0 = lane * 8; c0 < cols; c0 += 64 * 8 * U) {
+      typename Pack8<TS>::U vw[U], vm[U];
+      typename Pack8<TO>::U vo[U];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        vw.e[e] = update_w<TS>(vw.e[e], Store<TO>::to_f32(vo.e[e]), eta, u, decay != 0);
-        vm.e[e] = decay_round<TS>(mu, vm.e[e]);
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * 512;
+        if (c < cols) {
+          load8<TS>(vw[u], w + c);
+          load8<TS>(vm[u], mm + c);
+          load8<TO>(vo[u], o + c);
+        }
       }
-      store8<TS>(w + c, vw);
-      store8<TS>(mm + c, vm);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * 512;
+        if (c < cols) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            vw[u].e[e] = update_w<TS>(vw[u].e[e], Store<TO>::to_f32(vo[u].e[e]), eta, u_, decay != 0);
+            vm[u].e[e] = decay_round<TS>(mu, vm[u].e[e]);
+          }
+          store8<TS>(w + c, vw[u]);
+          store8<TS>(mm + c, vm[u]);
+        }
+      }
     }
   } else {
     for (int c = lane; c < cols; c += 64) {
-      w[c] = update_w<TS>(w[c], Store<TO>::to_f32(o[c]), eta, u, decay != 0);
+      w[c] = update_w<TS>(w[c], Store<TO>::to_f32(o[c]), eta, u_, decay != 0);
       mm[c] = decay_round<TS>(mu, mm[c]);
     }
   }
