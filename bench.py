@@ -1,11 +1,12 @@
 """Benchmark of the Dion3 optimizer step on one MI355X.
 
-A step is one call of dion3_step over the 7B-like transformer shape set
+A step is one call of dion3_step_deferred over the 7B-like transformer shape set
 (32 layers x {4 x 4096x4096, 2 x 4096x11008, 1 x 11008x4096}, bf16 W, M, G):
 momentum accumulation with l1 keys, top-k selection (k = ceil(f n), f = 1/4 by
 default), gather and Frobenius scaling, Gram Newton-Schulz in fp16 (T = 5,
 restart after iteration 2) batched over same-shape selected submatrices, and
-the fused update of W with error feedback on M.  Inputs are synthetic and
+the fused update of W; the error-feedback decay of the selected lines of M is
+applied by the next step's momentum pass (deferred, bit-identical).  Inputs are synthetic and
 resident in HBM before the timed region starts; the momentum state carries
 across steps.
 
@@ -84,9 +85,10 @@ def kernel_work(groups, ks, ns_bytes=2, store_bytes=2):
     """Algorithmic work per step of every kernel class of the library.
 
     Bytes: momentum_keys reads M, G and writes M (3 x storage bytes per
-    parameter); gather_scale reads each selected element and writes it in the
-    Newton-Schulz type; apply_update reads and writes W and M and reads O per
-    selected element.  FLOPs: a symmetric product counts only its lower
+    parameter; the deferred decay of the previous selection rides along);
+    gather_scale reads each selected element and writes it in the
+    Newton-Schulz type; apply_update reads and writes W and reads O per
+    selected element (the decay of M is deferred to the next momentum pass).  FLOPs: a symmetric product counts only its lower
     triangle (k(k+1)/2 entries, 2 x contraction length each); Q X is a full
     k x k by k x m product.  Returns {name: (kind, units per step)}."""
     w = {"momentum_keys": 0.0, "topk_select": 0.0, "gather_scale": 0.0, "apply_update": 0.0,
@@ -96,7 +98,7 @@ def kernel_work(groups, ks, ns_bytes=2, store_bytes=2):
         w["momentum_keys"] += b * rows * cols * 3 * store_bytes
         w["topk_select"] += b * n * 8 * 2
         w["gather_scale"] += b * k * m * (store_bytes + ns_bytes)
-        w["apply_update"] += b * k * m * (4 * store_bytes + ns_bytes)
+        w["apply_update"] += b * k * m * (2 * store_bytes + ns_bytes)
         tri = k * (k + 1) / 2
         passes, iters = 2, 5                     # restart after iteration 2
         w["syrk"] += b * passes * tri * 2 * m
@@ -163,8 +165,10 @@ def run_step_bench(d, synth, torch, args):
     print(f"# {args.set} set f={args.f:g}: groups {groups} k {ks}; workspace "
           f"{plan.ws.numel() / 2**30:.2f} GiB", file=sys.stderr, flush=True)
 
-    for _ in range(args.warmup):
-        plan.step(eta, 0.0, MU)
+    # deferred error feedback: each step's momentum pass applies the decay the
+    # previous step's selection owes (bit-identical to decaying in the update)
+    for w in range(args.warmup):
+        plan.step_deferred(eta, 0.0, MU, has_prev=w > 0)
     torch.cuda.synchronize()
     print("# warmup done", file=sys.stderr, flush=True)
 
@@ -175,7 +179,7 @@ def run_step_bench(d, synth, torch, args):
     torch.cuda.synchronize()
     start.record()
     for _ in range(args.steps):
-        plan.step(eta, 0.0, MU)
+        plan.step_deferred(eta, 0.0, MU, has_prev=args.warmup > 0 or _ > 0)
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps

@@ -104,6 +104,21 @@ int dion3_momentum_rowsel(const dion3_group* g, void* M, const void* G, int k,
                           int32_t* idx, double* keys, double* sel_sqnorm,
                           void* ws, size_t ws_bytes, void* stream);
 
+/* Deferred error feedback (Section 6 decays the selected lines of M by mu after
+ * the update; this entry point applies that decay at the start of the next
+ * step instead, inside the same pass over M).  As dion3_momentum_rowsel, and in
+ * addition, when prev_idx is not NULL, every canonical line listed in prev_idx
+ * ([batch][prev_k] ascending, the previous step's selection) is first decayed:
+ *   M <- round(round(mu * M) + G)        on those lines,
+ *   M <- round(M + G)                    on the others,
+ * which is bit-identical to decaying after the previous step and accumulating
+ * now.  prev_idx may alias idx (it is read before idx is written).  mu is fp32;
+ * the product is rounded once. */
+int dion3_momentum_rowsel_ef(const dion3_group* g, void* M, const void* G, int k,
+                             int32_t* idx, double* keys, double* sel_sqnorm,
+                             const int32_t* prev_idx, int prev_k, float mu,
+                             void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------- gather + scale */
 
 /* X[b] = M[b][S_b, :] / (sqrt(sel_sqnorm[b]) + eps) in canonical orientation
@@ -166,10 +181,18 @@ int dion3_gemm(int batch, int k, int m, int in_dtype, const void* Q, long long s
  *                     M <- round(mu * M)              (exact product, one rounding)
  *   other lines:      W <- round(a) if wd != 0, M untouched.
  *   O   [batch] slices of [k][m] (o_stride elements apart), canonical
- *       orientation, o_dtype DION3_F16 or DION3_F32.  eta, wd, mu are fp32. */
+ *       orientation, o_dtype DION3_F16 or DION3_F32.  eta, wd, mu are fp32.
+ *   M may be NULL: W is updated and the decay of M[S,:] is left to the caller
+ *   (deferred error feedback, see dion3_momentum_rowsel_ef / dion3_decay_rows). */
 int dion3_apply_rows(const dion3_group* g, void* W, void* M, const int32_t* idx, int k,
                      const void* O, int o_dtype, long long o_stride,
                      float eta, float wd, float mu, void* stream);
+
+/* The error-feedback decay alone, M[S,:] <- round(mu * M[S,:]) for the lines
+ * in idx ([batch][k] ascending), one rounding (Section 6).  Completes a
+ * deferred decay, e.g. before M is read or saved. */
+int dion3_decay_rows(const dion3_group* g, void* M, const int32_t* idx, int k, float mu,
+                     void* stream);
 
 /* ------------------------------------------------------------ whole step */
 
@@ -189,6 +212,18 @@ int dion3_step(int n_groups, const dion3_group* groups, void* const* W, void* co
                const void* const* G, const int* k, int32_t* const* idx,
                const dion3_ns_params* p, float eta, float wd, float mu,
                void* ws, size_t ws_bytes, void* stream);
+
+/* dion3_step with deferred error feedback: the decay of each step's selected
+ * lines is applied by the next step's momentum pass, so the update never
+ * touches M.  On entry idx[i] holds the previous step's selection when
+ * has_prev != 0 (it is decayed, then overwritten by this step's selection);
+ * pass has_prev = 0 on the first step.  After a call, M[i] still owes the
+ * decay of the lines in idx[i]: dion3_decay_rows completes it.  The sequence
+ * of W, M (once completed) and idx is bit-identical to dion3_step's. */
+int dion3_step_deferred(int n_groups, const dion3_group* groups, void* const* W, void* const* M,
+                        const void* const* G, const int* k, int32_t* const* idx, int has_prev,
+                        const dion3_ns_params* p, float eta, float wd, float mu,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------ measurement */
 

@@ -51,6 +51,17 @@ __device__ __forceinline__ bf16_t f64_to_bf16(double d) {
   return (bf16_t)(__float_as_uint((float)q) >> 16);
 }
 
+// ------------------------------------------------------- sorted index sets
+// First position in a[0..n) (ascending) whose value is >= v.
+__device__ __forceinline__ int lower_bound_i32(const int32_t* a, int n, int v) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] < v) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
 template <typename T> struct Store;
 template <> struct Store<float> {
   __device__ static float to_f32(float v) { return v; }
@@ -64,6 +75,14 @@ template <> struct Store<bf16_t> {
   __device__ static float to_f32(bf16_t v) { return bf16_to_f32(v); }
   __device__ static bf16_t from_f32(float v) { return f32_to_bf16(v); }
 };
+
+// mu * m rounded once to the storage type (the product of an fp32 and a bf16
+// value is exact in fp64; one round-to-nearest-even to bf16 follows).
+template <typename T> __device__ __forceinline__ T decay_round(float mu, T m);
+template <> __device__ __forceinline__ bf16_t decay_round<bf16_t>(float mu, bf16_t m) {
+  return f64_to_bf16((double)mu * (double)bf16_to_f32(m));
+}
+template <> __device__ __forceinline__ float decay_round<float>(float mu, float m) { return mu * m; }
 
 // ------------------------------------------------------------- reductions
 __device__ __forceinline__ double wave_sum(double v) {

@@ -37,16 +37,30 @@ __device__ __forceinline__ T add_round(T m, T g) {
   return Store<T>::from_f32(Store<T>::to_f32(m) + Store<T>::to_f32(g));
 }
 
+// M + G, after the pending error-feedback decay when `dec`: round(round(mu M) + G)
+template <typename T>
+__device__ __forceinline__ T accumulate(T m, T g, bool dec, float mu) {
+  return add_round(dec ? decay_round<T>(mu, m) : m, g);
+}
+
 // ------------------------------------------------------------- row selection
 template <typename T, bool VEC>
 __global__ __launch_bounds__(256) void momentum_rows_kernel(
     T* __restrict__ M, const T* __restrict__ G, int rows, int cols, long long bstride,
-    double* __restrict__ pkey, double* __restrict__ psq) {
+    double* __restrict__ pkey, double* __restrict__ psq, const int32_t* __restrict__ pidx, int pk,
+    float mu) {
   constexpr int V = Vec<T>::N;
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r0 = (blockIdx.x * 4 + wave) * kRowsPerWave;
   for (int r = r0; r < r0 + kRowsPerWave && r < rows; ++r) {
+    // was this row selected by the previous step (decay still pending)?
+    bool dec = false;
+    if (pidx) {
+      const int32_t* pb = pidx + (long long)b * pk;
+      const int pos = lower_bound_i32(pb, pk, r);
+      dec = pos < pk && pb[pos] == r;
+    }
     T* mr = M + b * bstride + (long long)r * cols;
     const T* gr = G + b * bstride + (long long)r * cols;
     double s1 = 0.0, s2 = 0.0;
@@ -71,7 +85,7 @@ __global__ __launch_bounds__(256) void momentum_rows_kernel(
             ug.v = vg[u];
 #pragma unroll
             for (int e = 0; e < (int)(16 / sizeof(T)); ++e) {
-              const T x = add_round(um.e[e], ug.e[e]);
+              const T x = accumulate(um.e[e], ug.e[e], dec, mu);
               um.e[e] = x;
               const double d = (double)Store<T>::to_f32(x);
               s1 += fabs(d);
@@ -83,7 +97,7 @@ __global__ __launch_bounds__(256) void momentum_rows_kernel(
       }
     } else {
       for (int c = lane; c < cols; c += 64) {
-        const T x = add_round(mr[c], gr[c]);
+        const T x = accumulate(mr[c], gr[c], dec, mu);
         mr[c] = x;
         const double d = (double)Store<T>::to_f32(x);
         s1 += fabs(d);
@@ -104,13 +118,33 @@ __global__ __launch_bounds__(256) void momentum_rows_kernel(
 template <typename T, bool VEC>
 __global__ __launch_bounds__(256) void momentum_cols_kernel(
     T* __restrict__ M, const T* __restrict__ G, int rows, int cols, long long bstride,
-    double* __restrict__ pkey, double* __restrict__ psq) {
+    double* __restrict__ pkey, double* __restrict__ psq, const int32_t* __restrict__ pidx, int pk,
+    float mu) {
   constexpr int E = 8;   // columns per lane
   __shared__ double red[2][4][kColBlock];
+  __shared__ uint32_t dmask[kColBlock / 32];   // columns of this block selected last step
   const int b = blockIdx.z, chunk = blockIdx.y, nchunks = gridDim.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // VEC: 8 contiguous columns per lane; otherwise columns lane + 64 e.
   auto col_of = [&](int e) { return blockIdx.x * kColBlock + (VEC ? lane * E + e : lane + 64 * e); };
+  const int cb = blockIdx.x * kColBlock;
+  if (threadIdx.x < kColBlock / 32) dmask[threadIdx.x] = 0u;
+  __syncthreads();
+  if (pidx) {
+    const int32_t* pb = pidx + (long long)b * pk;
+    const int lo = lower_bound_i32(pb, pk, cb), hi = lower_bound_i32(pb, pk, cb + kColBlock);
+    for (int t = lo + threadIdx.x; t < hi; t += 256) {
+      const unsigned lc = (unsigned)(pb[t] - cb);
+      if (lc < (unsigned)kColBlock) atomicOr(&dmask[lc >> 5], 1u << (lc & 31));
+    }
+  }
+  __syncthreads();
+  bool dec[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int lc = col_of(e) - cb;
+    dec[e] = (dmask[lc >> 5] >> (lc & 31)) & 1u;
+  }
   double s1[E], s2[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) s1[e] = s2[e] = 0.0;
@@ -133,7 +167,7 @@ __global__ __launch_bounds__(256) void momentum_cols_kernel(
         }
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const T x = add_round(um.e[e], ug.e[e]);
+          const T x = accumulate(um.e[e], ug.e[e], dec[e], mu);
           um.e[e] = x;
           const double d = (double)Store<T>::to_f32(x);
           s1[e] += fabs(d);
@@ -148,7 +182,7 @@ __global__ __launch_bounds__(256) void momentum_cols_kernel(
       for (int e = 0; e < E; ++e) {
         const int c = col_of(e);
         if (c < cols) {
-          const T x = add_round(mr[c], gr[c]);
+          const T x = accumulate(mr[c], gr[c], dec[e], mu);
           mr[c] = x;
           const double d = (double)Store<T>::to_f32(x);
           s1[e] += fabs(d);
@@ -293,7 +327,8 @@ static int nchunks_for(int axis, int rows) {
 
 template <typename T>
 static void launch_momentum(const dion3_group* g, int axis, void* M, const void* G,
-                            double* pkey, double* psq, hipStream_t s) {
+                            double* pkey, double* psq, const int32_t* pidx, int pk, float mu,
+                            hipStream_t s) {
   constexpr int V = Vec<T>::N;
   const bool vec = g->cols % V == 0 && (g->batch == 1 || g->batch_stride % V == 0) &&
                    aligned16(M) && aligned16(G);
@@ -302,19 +337,19 @@ static void launch_momentum(const dion3_group* g, int axis, void* M, const void*
     dim3 grid((g->rows + 4 * kRowsPerWave - 1) / (4 * kRowsPerWave), g->batch);
     if (vec)
       hipLaunchKernelGGL((momentum_rows_kernel<T, true>), grid, dim3(256), 0, s, (T*)M, (const T*)G,
-                         g->rows, g->cols, g->batch_stride, pkey, psq);
+                         g->rows, g->cols, g->batch_stride, pkey, psq, pidx, pk, mu);
     else
       hipLaunchKernelGGL((momentum_rows_kernel<T, false>), grid, dim3(256), 0, s, (T*)M, (const T*)G,
-                         g->rows, g->cols, g->batch_stride, pkey, psq);
+                         g->rows, g->cols, g->batch_stride, pkey, psq, pidx, pk, mu);
   } else {
     const bool vec8 = vec && g->cols % 8 == 0;
     dim3 grid((g->cols + kColBlock - 1) / kColBlock, nchunks_for(1, g->rows), g->batch);
     if (vec8)
       hipLaunchKernelGGL((momentum_cols_kernel<T, true>), grid, dim3(256), 0, s, (T*)M, (const T*)G,
-                         g->rows, g->cols, g->batch_stride, pkey, psq);
+                         g->rows, g->cols, g->batch_stride, pkey, psq, pidx, pk, mu);
     else
       hipLaunchKernelGGL((momentum_cols_kernel<T, false>), grid, dim3(256), 0, s, (T*)M, (const T*)G,
-                         g->rows, g->cols, g->batch_stride, pkey, psq);
+                         g->rows, g->cols, g->batch_stride, pkey, psq, pidx, pk, mu);
   }
 }
 
@@ -330,12 +365,14 @@ extern "C" size_t dion3_rowsel_workspace_bytes(const dion3_group* g) {
   return bytes < 256 ? 256 : bytes;
 }
 
-extern "C" int dion3_momentum_rowsel(const dion3_group* g, void* M, const void* G, int k,
-                                     int32_t* idx, double* keys, double* sel_sqnorm,
-                                     void* ws, size_t ws_bytes, void* stream) {
+extern "C" int dion3_momentum_rowsel_ef(const dion3_group* g, void* M, const void* G, int k,
+                                        int32_t* idx, double* keys, double* sel_sqnorm,
+                                        const int32_t* prev_idx, int prev_k, float mu,
+                                        void* ws, size_t ws_bytes, void* stream) {
   int n, m, axis;
   if (!canonical_dims(g, &n, &m, &axis)) return DION3_ERR_INVALID_ARG;
   if (!M || !G || !idx || k < 1 || k > n) return DION3_ERR_INVALID_ARG;
+  if (prev_idx && (prev_k < 1 || prev_k > n)) return DION3_ERR_INVALID_ARG;
   if (g->dtype != DION3_F32 && g->dtype != DION3_BF16) return DION3_ERR_INVALID_ARG;
   if (n > kTopkThreads * kTopkPer) return DION3_ERR_UNSUPPORTED;
   const size_t need = dion3_rowsel_workspace_bytes(g);
@@ -345,9 +382,9 @@ extern "C" int dion3_momentum_rowsel(const dion3_group* g, void* M, const void* 
   double* pkey = (double*)ws;
   double* psq = pkey + (size_t)g->batch * nch * n;
   if (g->dtype == DION3_BF16)
-    launch_momentum<bf16_t>(g, axis, M, G, pkey, psq, s);
+    launch_momentum<bf16_t>(g, axis, M, G, pkey, psq, prev_idx, prev_k, mu, s);
   else
-    launch_momentum<float>(g, axis, M, G, pkey, psq, s);
+    launch_momentum<float>(g, axis, M, G, pkey, psq, prev_idx, prev_k, mu, s);
   int st = launch_status();
   if (st) return st;
   {
@@ -356,4 +393,11 @@ extern "C" int dion3_momentum_rowsel(const dion3_group* g, void* M, const void* 
                        idx, keys, sel_sqnorm);
   }
   return launch_status();
+}
+
+extern "C" int dion3_momentum_rowsel(const dion3_group* g, void* M, const void* G, int k,
+                                     int32_t* idx, double* keys, double* sel_sqnorm,
+                                     void* ws, size_t ws_bytes, void* stream) {
+  return dion3_momentum_rowsel_ef(g, M, G, k, idx, keys, sel_sqnorm, nullptr, 0, 0.f, ws, ws_bytes,
+                                  stream);
 }

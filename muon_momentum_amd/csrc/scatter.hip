@@ -33,13 +33,6 @@ __device__ __forceinline__ void store8(T* p, const typename Pack8<T>::U& u) {
   for (int w = 0; w < (int)(8 * sizeof(T) / 16); ++w) ((uint4*)p)[w] = u.v[w];
 }
 
-// mu * m rounded once to the storage type (the product is exact in fp64).
-template <typename T> __device__ __forceinline__ T decay_round(float mu, T m);
-template <> __device__ __forceinline__ bf16_t decay_round<bf16_t>(float mu, bf16_t m) {
-  return f64_to_bf16((double)mu * (double)bf16_to_f32(m));
-}
-template <> __device__ __forceinline__ float decay_round<float>(float mu, float m) { return mu * m; }
-
 // w' = round(fp32(a - eta o)) with a = fp32(u w) when decaying, else w.
 template <typename T>
 __device__ __forceinline__ T update_w(T w, float o, float eta, float u, bool decay) {
@@ -128,15 +121,17 @@ __global__ __launch_bounds__(256) void apply_rows_kernel(
     TS* __restrict__ W, TS* __restrict__ M, long long bstride, int nlines, int cols,
     const int32_t* __restrict__ idx, int k, const TO* __restrict__ O, long long ostride, float eta,
     float u_, int decay, float mu) {
+  // W == nullptr: decay M only; M == nullptr: update W only (decay deferred)
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = blockIdx.x * 4 + wave;
   if (i >= k) return;
   const int r = idx[(long long)b * k + i];
   if (r < 0 || r >= nlines) return;
-  TS* w = W + b * bstride + (long long)r * cols;
-  TS* mm = M + b * bstride + (long long)r * cols;
-  const TO* o = O + b * ostride + (long long)i * cols;
+  const bool dw = W != nullptr, dm = M != nullptr;
+  TS* w = dw ? W + b * bstride + (long long)r * cols : nullptr;
+  TS* mm = dm ? M + b * bstride + (long long)r * cols : nullptr;
+  const TO* o = dw ? O + b * ostride + (long long)i * cols : nullptr;
   if (VEC) {
     // U chunks of 512 elements per wave in flight: all loads first, then stores
     constexpr int U = 4;
@@ -147,34 +142,38 @@ __global__ __launch_bounds__(256) void apply_rows_kernel(
       for (int u = 0; u < U; ++u) {
         const int c = c0 + u * 512;
         if (c < cols) {
-          load8<TS>(vw[u], w + c);
-          load8<TS>(vm[u], mm + c);
-          load8<TO>(vo[u], o + c);
+          if (dw) { load8<TS>(vw[u], w + c); load8<TO>(vo[u], o + c); }
+          if (dm) load8<TS>(vm[u], mm + c);
         }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int c = c0 + u * 512;
         if (c < cols) {
+          if (dw) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            vw[u].e[e] = update_w<TS>(vw[u].e[e], Store<TO>::to_f32(vo[u].e[e]), eta, u_, decay != 0);
-            vm[u].e[e] = decay_round<TS>(mu, vm[u].e[e]);
+            for (int e = 0; e < 8; ++e)
+              vw[u].e[e] = update_w<TS>(vw[u].e[e], Store<TO>::to_f32(vo[u].e[e]), eta, u_, decay != 0);
+            store8<TS>(w + c, vw[u]);
           }
-          store8<TS>(w + c, vw[u]);
-          store8<TS>(mm + c, vm[u]);
+          if (dm) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vm[u].e[e] = decay_round<TS>(mu, vm[u].e[e]);
+            store8<TS>(mm + c, vm[u]);
+          }
         }
       }
     }
   } else {
     for (int c = lane; c < cols; c += 64) {
-      w[c] = update_w<TS>(w[c], Store<TO>::to_f32(o[c]), eta, u_, decay != 0);
-      mm[c] = decay_round<TS>(mu, mm[c]);
+      if (dw) w[c] = update_w<TS>(w[c], Store<TO>::to_f32(o[c]), eta, u_, decay != 0);
+      if (dm) mm[c] = decay_round<TS>(mu, mm[c]);
     }
   }
 }
 
-// W[b][j][idx[i]] and M[b][j][idx[i]] for the canonical O[b][i][j]; grid (m/64, k/64, batch)
+// W[b][j][idx[i]] and M[b][j][idx[i]] for the canonical O[b][i][j]; grid (m/64, k/64, batch).
+// W == nullptr: decay M only; M == nullptr: update W only (decay deferred).
 template <typename TS, typename TO>
 __global__ __launch_bounds__(256) void apply_cols_kernel(
     TS* __restrict__ W, TS* __restrict__ M, long long bstride, int rows, int cols,
@@ -184,28 +183,31 @@ __global__ __launch_bounds__(256) void apply_cols_kernel(
   const int b = blockIdx.z;
   const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
   const int t = threadIdx.x;
-  const TO* Ob = O + b * ostride;
+  const bool dw = W != nullptr, dm = M != nullptr;
+  if (dw) {
+    const TO* Ob = O + b * ostride;
 #pragma unroll 4
-  for (int s = 0; s < 16; ++s) {
-    const int il2 = (t >> 6) + 4 * s;
-    const int jl = t & 63;
-    const int i = i0 + il2, j = j0 + jl;
-    tile[il2][jl] = (i < k && j < rows) ? Store<TO>::to_f32(Ob[(long long)i * rows + j]) : 0.f;
+    for (int s = 0; s < 16; ++s) {
+      const int il2 = (t >> 6) + 4 * s;
+      const int jl = t & 63;
+      const int i = i0 + il2, j = j0 + jl;
+      tile[il2][jl] = (i < k && j < rows) ? Store<TO>::to_f32(Ob[(long long)i * rows + j]) : 0.f;
+    }
   }
   __syncthreads();
   const int il = t & 63;
   const int col = i0 + il < k ? idx[(long long)b * k + i0 + il] : -1;
   if (col < 0 || col >= cols) return;
-  TS* Wb = W + b * bstride;
-  TS* Mb = M + b * bstride;
+  TS* Wb = dw ? W + b * bstride : nullptr;
+  TS* Mb = dm ? M + b * bstride : nullptr;
 #pragma unroll 4
   for (int s = 0; s < 16; ++s) {
     const int jj = (t >> 6) + 4 * s;
     const int j = j0 + jj;
     if (j < rows) {
       const long long off = (long long)j * cols + col;
-      Wb[off] = update_w<TS>(Wb[off], tile[il][jj], eta, u, decay != 0);
-      Mb[off] = decay_round<TS>(mu, Mb[off]);
+      if (dw) Wb[off] = update_w<TS>(Wb[off], tile[il][jj], eta, u, decay != 0);
+      if (dm) Mb[off] = decay_round<TS>(mu, Mb[off]);
     }
   }
 }
@@ -267,8 +269,8 @@ static void launch_apply(const dion3_group* g, int axis, int n, int m, void* W, 
   // u = fp32(1 - eta wd): the product is exact in fp64, one rounding to fp32
   const float u = (float)(1.0 - (double)eta * (double)wd);
   const int decay = wd != 0.0f;
-  TimedLaunch tl("apply_update", s);
-  if (decay) {
+  TimedLaunch tl(W ? "apply_update" : "decay_rows", s);
+  if (decay && W) {
     dim3 grid((g->rows + 7) / 8, g->batch);
     hipLaunchKernelGGL((decay_unselected_kernel<TS>), grid, dim3(256), 0, s, (TS*)W, g->batch_stride,
                        g->rows, g->cols, axis, n, idx, k, u);
@@ -320,7 +322,7 @@ extern "C" int dion3_apply_rows(const dion3_group* g, void* W, void* M, const in
                                 float mu, void* stream) {
   int n, m, axis;
   if (!canonical_dims(g, &n, &m, &axis)) return DION3_ERR_INVALID_ARG;
-  if (!W || !M || !idx || !O || k < 1 || k > n) return DION3_ERR_INVALID_ARG;
+  if (!W || !idx || !O || k < 1 || k > n) return DION3_ERR_INVALID_ARG;   // M may be NULL
   if (g->batch > 1 && o_stride < (long long)k * m) return DION3_ERR_INVALID_ARG;
   if (n > 32768) return DION3_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
@@ -332,6 +334,22 @@ extern "C" int dion3_apply_rows(const dion3_group* g, void* W, void* M, const in
     launch_apply<float, float>(g, axis, n, m, W, M, idx, k, O, o_stride, eta, wd, mu, s);
   else if (g->dtype == DION3_F32 && o_dtype == DION3_F16)
     launch_apply<float, f16>(g, axis, n, m, W, M, idx, k, O, o_stride, eta, wd, mu, s);
+  else
+    return DION3_ERR_INVALID_ARG;
+  return launch_status();
+}
+
+extern "C" int dion3_decay_rows(const dion3_group* g, void* M, const int32_t* idx, int k, float mu,
+                                void* stream) {
+  int n, m, axis;
+  if (!canonical_dims(g, &n, &m, &axis)) return DION3_ERR_INVALID_ARG;
+  if (!M || !idx || k < 1 || k > n) return DION3_ERR_INVALID_ARG;
+  if (n > 32768) return DION3_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  if (g->dtype == DION3_BF16)
+    launch_apply<bf16_t, bf16_t>(g, axis, n, m, nullptr, M, idx, k, nullptr, 0, 0.f, 0.f, mu, s);
+  else if (g->dtype == DION3_F32)
+    launch_apply<float, float>(g, axis, n, m, nullptr, M, idx, k, nullptr, 0, 0.f, 0.f, mu, s);
   else
     return DION3_ERR_INVALID_ARG;
   return launch_status();

@@ -54,10 +54,10 @@ extern "C" size_t dion3_step_workspace_bytes(int n_groups, const dion3_group* gr
   return P.rowsel + 2 * P.xbuf + P.gram;
 }
 
-extern "C" int dion3_step(int n_groups, const dion3_group* groups, void* const* W, void* const* M,
-                          const void* const* G, const int* k, int32_t* const* idx,
-                          const dion3_ns_params* p, float eta, float wd, float mu, void* ws,
-                          size_t ws_bytes, void* stream) {
+static int run_step(int n_groups, const dion3_group* groups, void* const* W, void* const* M,
+                    const void* const* G, const int* k, int32_t* const* idx,
+                    const dion3_ns_params* p, float eta, float wd, float mu, void* ws,
+                    size_t ws_bytes, void* stream, bool deferred, bool has_prev) {
   Plan P;
   if (!W || !M || !G || !idx || !make_plan(n_groups, groups, k, p, P)) return DION3_ERR_INVALID_ARG;
   for (int i = 0; i < n_groups; ++i)
@@ -79,7 +79,10 @@ extern "C" int dion3_step(int n_groups, const dion3_group* groups, void* const* 
       const dion3_group& gi = groups[i];
       const size_t rsz = al256(dion3_rowsel_workspace_bytes(&gi));
       double* sqn = (double*)(rs_ws + rsz);
-      st = dion3_momentum_rowsel(&gi, M[i], G[i], kk, idx[i], nullptr, sqn, rs_ws, rsz, stream);
+      // deferred error feedback: idx[i] holds the previous selection on entry;
+      // its decay is applied in this pass, then idx[i] is overwritten
+      st = dion3_momentum_rowsel_ef(&gi, M[i], G[i], kk, idx[i], nullptr, sqn,
+                                    deferred && has_prev ? idx[i] : nullptr, kk, mu, rs_ws, rsz, stream);
       if (st) return st;
       st = dion3_gather_rows(&gi, M[i], idx[i], kk, sqn, p->eps, p->ns_dtype, X0 + nb * slice, stream);
       if (st) return st;
@@ -90,11 +93,27 @@ extern "C" int dion3_step(int n_groups, const dion3_group* groups, void* const* 
     nb = 0;
     for (int i : c) {
       const dion3_group& gi = groups[i];
-      st = dion3_apply_rows(&gi, W[i], M[i], idx[i], kk, O + nb * slice, p->ns_dtype,
+      st = dion3_apply_rows(&gi, W[i], deferred ? nullptr : M[i], idx[i], kk, O + nb * slice, p->ns_dtype,
                             (long long)kk * mm, eta, wd, mu, stream);
       if (st) return st;
       nb += gi.batch;
     }
   }
   return st;
+}
+
+extern "C" int dion3_step(int n_groups, const dion3_group* groups, void* const* W, void* const* M,
+                          const void* const* G, const int* k, int32_t* const* idx,
+                          const dion3_ns_params* p, float eta, float wd, float mu, void* ws,
+                          size_t ws_bytes, void* stream) {
+  return run_step(n_groups, groups, W, M, G, k, idx, p, eta, wd, mu, ws, ws_bytes, stream, false, false);
+}
+
+extern "C" int dion3_step_deferred(int n_groups, const dion3_group* groups, void* const* W,
+                                   void* const* M, const void* const* G, const int* k,
+                                   int32_t* const* idx, int has_prev, const dion3_ns_params* p,
+                                   float eta, float wd, float mu, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  return run_step(n_groups, groups, W, M, G, k, idx, p, eta, wd, mu, ws, ws_bytes, stream, true,
+                  has_prev != 0);
 }

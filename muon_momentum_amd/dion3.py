@@ -58,6 +58,10 @@ def _load() -> ctypes.CDLL:
         "dion3_status_string": (ctypes.c_char_p, [i]),
         "dion3_rowsel_workspace_bytes": (sz, [gp]),
         "dion3_momentum_rowsel": (i, [gp, vp, vp, i, vp, vp, vp, vp, sz, vp]),
+        "dion3_momentum_rowsel_ef": (i, [gp, vp, vp, i, vp, vp, vp, vp, i, f, vp, sz, vp]),
+        "dion3_decay_rows": (i, [gp, vp, vp, i, f, vp]),
+        "dion3_step_deferred": (i, [i, gp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                    ctypes.POINTER(i), ctypes.POINTER(vp), i, pp, f, f, f, vp, sz, vp]),
         "dion3_gather_rows": (i, [gp, vp, vp, i, vp, f, i, vp, vp]),
         "dion3_gram_ns_workspace_bytes": (sz, [i, i, i, i]),
         "dion3_gram_ns": (i, [i, i, i, pp, vp, vp, vp, sz, vp]),
@@ -158,6 +162,21 @@ def dion3_momentum_rowsel(M, G, k, idx, keys=None, sel_sqnorm=None, ws=None, sel
            "dion3_momentum_rowsel")
 
 
+def dion3_momentum_rowsel_ef(M, G, k, idx, prev_idx, prev_k, mu, keys=None, sel_sqnorm=None, ws=None,
+                             sel_axis=-1):
+    g = make_group(M, sel_axis)
+    if ws is None:
+        ws = workspace(dion3_rowsel_workspace_bytes(g), M.device)
+    _check(lib.dion3_momentum_rowsel_ef(ctypes.byref(g), _ptr(M), _ptr(G), k, _ptr(idx), _ptr(keys),
+                                        _ptr(sel_sqnorm), _ptr(prev_idx), prev_k, mu, _ptr(ws), ws.numel(),
+                                        _stream()), "dion3_momentum_rowsel_ef")
+
+
+def dion3_decay_rows(M, idx, k, mu, sel_axis=-1):
+    g = make_group(M, sel_axis)
+    _check(lib.dion3_decay_rows(ctypes.byref(g), _ptr(M), _ptr(idx), k, mu, _stream()), "dion3_decay_rows")
+
+
 def dion3_gather_rows(M, idx, k, sel_sqnorm, X, eps=DEFAULT_EPS, sel_axis=-1):
     g = make_group(M, sel_axis)
     _check(lib.dion3_gather_rows(ctypes.byref(g), _ptr(M), _ptr(idx), k, _ptr(sel_sqnorm), eps,
@@ -232,6 +251,21 @@ class StepPlan:
         _check(lib.dion3_step(self.n, self.groups, self.W, self.M, self.G, self.k, self.idx,
                               ctypes.byref(self.params), eta, wd, mu, _ptr(self.ws), self.ws.numel(),
                               _stream()), "dion3_step")
+
+    def step_deferred(self, eta, wd, mu, has_prev):
+        """dion3_step_deferred: the idx tensors carry the previous selection in
+        (has_prev) and this step's selection out; M owes its decay until the
+        next step or flush_decay()."""
+        _check(lib.dion3_step_deferred(self.n, self.groups, self.W, self.M, self.G, self.k, self.idx,
+                                       1 if has_prev else 0, ctypes.byref(self.params), eta, wd, mu,
+                                       _ptr(self.ws), self.ws.numel(), _stream()), "dion3_step_deferred")
+
+    def flush_decay(self, mu):
+        """Complete the pending decay of the last deferred step on every group."""
+        Ws, Ms, Gs, idxs = self._keep
+        for M, idx, k, g in zip(Ms, idxs, self.k, self.groups):
+            _check(lib.dion3_decay_rows(ctypes.byref(g), _ptr(M), _ptr(idx), k, mu, _stream()),
+                   "dion3_decay_rows")
 
 
 def dion3_step(Ws, Ms, Gs, ks, idxs, eta, wd, mu, params=None, sel_axes=None):

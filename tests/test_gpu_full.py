@@ -124,3 +124,42 @@ def test_14b_three_steps(d):
     groups = synth.shape_groups("14b")
     worst = run_set(d, "14b", 0.25, 3, {0: [0], 2: [groups[2][2] - 1]})
     print(f"14b f=1/4 three steps worst O error {worst:.2e}")
+
+
+def test_7b_deferred_matches_immediate(d):
+    """The benchmark's deferred-decay step at full 7B size (f = 1/4) against
+    the immediate step over two steps: indices and W bit for bit after each
+    step, M bit for bit once the pending decay is completed."""
+    groups = synth.shape_groups("7b")
+    ks = [d.dion3_k_from_fraction(min(r, c), 0.25) for r, c, _ in groups]
+    mu, eta = 0.95, 0.04
+    params = d.make_ns_params(ns_dtype=d.F16)
+    sets = []
+    for _ in range(2):
+        Ws, Ms, Gs, ids = [], [], [], []
+        for gi, (r, c, b) in enumerate(groups):
+            Ws.append(synth.weights(r, c, b, dtype="bf16", device=DEV, group_seed=gi))
+            Gs.append(synth.gradient(r, c, b, dtype="bf16", device=DEV, group_seed=gi, step=0))
+            Ms.append(torch.zeros(b, r, c, dtype=torch.bfloat16, device=DEV))
+            ids.append(torch.empty(b, ks[gi], dtype=torch.int32, device=DEV))
+        sets.append((Ws, Ms, Gs, ids, d.StepPlan(Ws, Ms, Gs, ks, ids, params)))
+    (Wa, Ma, Ga, ia, pa), (Wb, Mb, Gb, ib, pb) = sets
+    for step in range(2):
+        if step:
+            for gi, (r, c, b) in enumerate(groups):
+                Gn = synth.gradient(r, c, b, dtype="bf16", device=DEV, group_seed=gi, step=step)
+                Ga[gi].copy_(Gn)
+                Gb[gi].copy_(Gn)
+                del Gn
+        pa.step(eta, 0.0, mu)
+        pb.step_deferred(eta, 0.0, mu, has_prev=step > 0)
+        torch.cuda.synchronize()
+        for gi in range(len(groups)):
+            assert torch.equal(ia[gi], ib[gi]), (step, gi)
+            assert torch.equal(Wa[gi].view(torch.int16), Wb[gi].view(torch.int16)), (step, gi)
+    pb.flush_decay(mu)
+    torch.cuda.synchronize()
+    for gi in range(len(groups)):
+        assert torch.equal(Ma[gi].view(torch.int16), Mb[gi].view(torch.int16)), gi
+    del sets, Wa, Ma, Ga, Wb, Mb, Gb, pa, pb
+    torch.cuda.empty_cache()

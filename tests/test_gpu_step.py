@@ -112,3 +112,57 @@ def test_step_deterministic(d):
         res.append([bits(g[0]) for g in A] + [bits(g[1]) for g in A] + [i.cpu().numpy() for i in idx])
     for a, b in zip(*res):
         assert np.array_equal(a, b)
+
+
+def test_deferred_decay_matches_immediate(d):
+    """dion3_step_deferred over three steps reproduces dion3_step bit for bit:
+    indices and W after every step, M once the pending decay is completed."""
+    shapes = [(128, 512, 3), (512, 128, 2), (256, 256, 2)]
+    dt, f = "bf16", 0.25
+    mu, eta = 0.95, 0.04
+    params = d.make_ns_params(ns_dtype=d.F16)
+    ks = [d.dion3_k_from_fraction(min(r, c), f) for r, c, _ in shapes]
+    A = _groups(shapes, dt, step=0, seed0=30)
+    B = [(W.clone(), M.clone(), G.clone()) for W, M, G in A]
+    idx_a = [torch.empty(b, k, dtype=torch.int32, device=DEV) for (_, _, b), k in zip(shapes, ks)]
+    idx_b = [torch.empty(b, k, dtype=torch.int32, device=DEV) for (_, _, b), k in zip(shapes, ks)]
+    pa = d.StepPlan([g[0] for g in A], [g[1] for g in A], [g[2] for g in A], ks, idx_a, params)
+    pb = d.StepPlan([g[0] for g in B], [g[1] for g in B], [g[2] for g in B], ks, idx_b, params)
+    for step in range(3):
+        for gi, (r, c, b) in enumerate(shapes):
+            Gn = synth.gradient(r, c, b, dtype=dt, device=DEV, group_seed=30 + gi, step=step + 1)
+            A[gi][2].copy_(Gn)
+            B[gi][2].copy_(Gn)
+        pa.step(eta, 0.0, mu)
+        pb.step_deferred(eta, 0.0, mu, has_prev=step > 0)
+        torch.cuda.synchronize()
+        for gi in range(len(shapes)):
+            assert np.array_equal(idx_a[gi].cpu().numpy(), idx_b[gi].cpu().numpy()), (step, gi)
+            assert np.array_equal(bits(A[gi][0]), bits(B[gi][0])), (step, gi)
+            Mb = B[gi][1].clone()
+            d.dion3_decay_rows(Mb, idx_b[gi], ks[gi], mu)
+            torch.cuda.synchronize()
+            assert np.array_equal(bits(A[gi][1]), bits(Mb)), (step, gi)
+
+
+def test_momentum_ef_against_oracle(d):
+    """M <- round(round(mu M) + G) on the previous selection, round(M + G) elsewhere."""
+    for rows, cols, axis in [(300, 1000, 0), (900, 260, 1)]:
+        n = rows if axis == 0 else cols
+        kp = n // 4
+        M = synth.gradient(rows, cols, 2, dtype="bf16", device=DEV, group_seed=3, step=5)
+        G = synth.gradient(rows, cols, 2, dtype="bf16", device=DEV, group_seed=4, step=6)
+        rng = np.random.default_rng(rows)
+        prev = np.stack([np.sort(rng.choice(n, kp, replace=False)) for _ in range(2)]).astype(np.int32)
+        Mh, Gh = to64(M), to64(G)
+        idx = torch.empty(2, kp, dtype=torch.int32, device=DEV)
+        d.dion3_momentum_rowsel_ef(M, G, kp, idx, torch.from_numpy(prev).to(DEV), kp, 0.95)
+        torch.cuda.synchronize()
+        for b in range(2):
+            Mc = Mh[b] if axis == 0 else Mh[b].T
+            Gc = Gh[b] if axis == 0 else Gh[b].T
+            dec = Mc.copy()
+            dec[prev[b]] = O.round_to(O.f32(0.95) * Mc[prev[b]], "bf16")
+            ref = O.momentum_accumulate(dec, Gc, "bf16")
+            ref = ref if axis == 0 else ref.T
+            assert np.array_equal(bits(M[b]), np_bits(ref, torch.bfloat16)), (rows, cols, b)
