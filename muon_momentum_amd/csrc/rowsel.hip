@@ -10,7 +10,7 @@
 // the fp64 sums of |M| (the key) and M^2 (for the Frobenius norm of the
 // selected submatrix).  Row selection: one wave per row, lane-sequential
 // accumulation then a butterfly reduction.  Column selection: a work-group
-// owns 512 columns x 256 rows; each lane owns 8 columns; the four waves are
+// owns 512 columns x 1024 rows; each lane owns 8 columns; the four waves are
 // combined in a fixed order and written as per-chunk partial sums.
 // Kernel 2 (one work-group per matrix): sums the partials in chunk order,
 // radix-selects the k-th largest key on its 64-bit pattern (non-negative
@@ -23,7 +23,7 @@
 namespace dion3 {
 
 constexpr int kColBlock = 512;     // columns per work-group (column selection)
-constexpr int kChunkRows = 256;    // rows per work-group (column selection)
+constexpr int kChunkRows = 1024;   // rows per work-group (column selection)
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkPer = 32;       // keys per thread -> n <= 32768
 constexpr int kRowsPerWave = 2;
@@ -31,6 +31,19 @@ constexpr int kRowsPerWave = 2;
 template <typename T> struct Vec;
 template <> struct Vec<bf16_t> { static constexpr int N = 8; };
 template <> struct Vec<float> { static constexpr int N = 4; };
+
+// 16-byte streaming accesses of the momentum pass: every byte of M and G is
+// touched once per step, so the loads and stores are non-temporal and do not
+// displace anything worth keeping in the caches.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_stream(void* p, uint4 v) {
+  u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, (u32x4*)p);
+}
 
 template <typename T>
 __device__ __forceinline__ T add_round(T m, T g) {
@@ -72,8 +85,8 @@ __global__ __launch_bounds__(256) void momentum_rows_kernel(
         for (int u = 0; u < U; ++u) {
           const int c = c0 + u * 64 * V;
           if (c < cols) {
-            vm[u] = *(const uint4*)(mr + c);
-            vg[u] = *(const uint4*)(gr + c);
+            vm[u] = ld_stream(mr + c);
+            vg[u] = ld_stream(gr + c);
           }
         }
 #pragma unroll
@@ -91,7 +104,7 @@ __global__ __launch_bounds__(256) void momentum_rows_kernel(
               s1 += fabs(d);
               s2 += d * d;
             }
-            *(uint4*)(mr + c) = um.v;
+            st_stream(mr + c, um.v);
           }
         }
       }
@@ -162,8 +175,8 @@ __global__ __launch_bounds__(256) void momentum_cols_kernel(
         union { uint4 v[E * sizeof(T) / 16]; T e[E]; } um, ug;
 #pragma unroll
         for (int w = 0; w < (int)(E * sizeof(T) / 16); ++w) {
-          um.v[w] = *(const uint4*)(mr + c + w * (16 / sizeof(T)));
-          ug.v[w] = *(const uint4*)(gr + c + w * (16 / sizeof(T)));
+          um.v[w] = ld_stream(mr + c + w * (16 / sizeof(T)));
+          ug.v[w] = ld_stream(gr + c + w * (16 / sizeof(T)));
         }
 #pragma unroll
         for (int e = 0; e < E; ++e) {
@@ -175,7 +188,7 @@ __global__ __launch_bounds__(256) void momentum_cols_kernel(
         }
 #pragma unroll
         for (int w = 0; w < (int)(E * sizeof(T) / 16); ++w)
-          *(uint4*)(mr + c + w * (16 / sizeof(T))) = um.v[w];
+          st_stream(mr + c + w * (16 / sizeof(T)), um.v[w]);
       }
     } else {
 #pragma unroll
@@ -270,14 +283,33 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
         atomicAdd(&hist[(unsigned)(u[j] >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (t == 0) {
-      int acc = 0, d = 255;
-      for (; d > 0; --d) {
-        if (acc + (int)hist[d] >= krem) break;
-        acc += (int)hist[d];
+    if (t < 64) {
+      // wave 0: lane l owns digits 255 - 4l .. 252 - 4l; a suffix scan over
+      // the lanes finds the digit where the count from the top reaches krem
+      const int d0 = 255 - 4 * t;
+      const int c0 = (int)hist[d0], c1 = (int)hist[d0 - 1], c2 = (int)hist[d0 - 2], c3 = (int)hist[d0 - 3];
+      const int mine = c0 + c1 + c2 + c3;
+      int incl = mine;                                   // inclusive prefix over lanes 0..t
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off, 64);
+        if (t >= off) incl += v;
       }
-      s_digit = d;
-      s_krem = krem - acc;
+      const int before = incl - mine;
+      const unsigned long long hit = __ballot(incl >= krem);
+      const int lane_hit = hit ? __ffsll((long long)hit) - 1 : 63;
+      if (t == lane_hit) {
+        int acc = before, d = d0;
+        const int cs[4] = {c0, c1, c2, c3};
+        int q = 0;
+        for (; q < 3; ++q) {
+          if (acc + cs[q] >= krem) break;
+          acc += cs[q];
+        }
+        d = d0 - q;
+        s_digit = d;
+        s_krem = krem - acc;
+      }
     }
     __syncthreads();
     prefix |= (uint64_t)s_digit << shift;
