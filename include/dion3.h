@@ -208,14 +208,17 @@ size_t dion3_step_workspace_bytes(int n_groups, const dion3_group* groups, const
  * dion3_apply_rows.  W[i], M[i], G[i] are the group tensors, idx[i] receives
  * the [batch][k[i]] selected indices.  eta, wd, mu as in dion3_apply_rows
  * (one value for all groups).
- * Streams: the momentum passes and the updates are enqueued on `stream`; the
- * gathers and the Newton-Schulz products run on a side stream of the current
- * device that the library creates (with an event pool) on the device's first
- * step and keeps until the process ends, ordered against `stream` by events.
- * When the call returns, everything it enqueued is ordered before later work
- * on `stream`, as if all of it had been enqueued there; `stream` must belong
- * to the current device.  Concurrent calls on one device are serialised while
- * they enqueue.  The workspace (dion3_step_workspace_bytes) holds the selected
+ * Streams: the first class's momentum pass and the last class's update are
+ * enqueued on `stream`; the gathers and Newton-Schulz products run on a side
+ * stream, and the other momentum passes and updates on a stream limited to
+ * half of the compute units, so that they overlap another class's products.
+ * Both library streams belong to the current device; the library creates them
+ * (with an event pool) on the device's first step and keeps them until the
+ * process ends.  Events order all three against `stream`: when the call
+ * returns, everything it enqueued is ordered before later work on `stream`,
+ * as if all of it had been enqueued there; `stream` must belong to the
+ * current device.  Concurrent calls on one device are serialised while they
+ * enqueue.  The workspace (dion3_step_workspace_bytes) holds the selected
  * sums of squares of every group and, with two or more (k, m) classes, two
  * Newton-Schulz outputs so that one class's update overlaps the next class. */
 int dion3_step(int n_groups, const dion3_group* groups, void* const* W, void* const* M,

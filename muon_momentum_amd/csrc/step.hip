@@ -8,15 +8,18 @@
 // up-projection group (row selection) and a down-projection group (column
 // selection, stored transposed) run their Newton-Schulz together.
 //
-// Two streams.  The HBM-bound passes (momentum + selection of every group,
-// then the update of each class) run on the caller's stream; the gathers and
-// the matrix-core-bound Newton-Schulz chain of each class run on a side
-// stream owned by the library, so the momentum pass of later classes and the
-// update of earlier ones overlap the products of the current class.  Events
-// order the two: class c's gather waits for its groups' selection, class c's
-// update waits for its Newton-Schulz, and the caller's stream ends the call
-// having waited for all side-stream work.  Every kernel computes exactly what
-// it computes on one stream, so the results do not depend on the overlap.
+// Three streams.  The gathers and the matrix-core-bound Newton-Schulz chain
+// of each class run on a side stream owned by the library.  The first class's
+// momentum + selection pass and the last class's update have nothing to
+// overlap and run on the caller's stream over the whole chip; the momentum
+// passes of the other classes and the updates of all but the last run on a
+// second library stream restricted to half of the compute units (spread
+// evenly over the XCDs), so that these HBM-bound passes overlap the products
+// of another class without taking every compute unit from them.  Events order
+// the streams: class c's gather waits for its groups' selection, class c's
+// update for its Newton-Schulz, and the caller's stream ends the call having
+// waited for all library-stream work.  Every kernel computes exactly what it
+// computes on one stream, so the results do not depend on the overlap.
 #include <mutex>
 #include <vector>
 
@@ -59,17 +62,32 @@ static bool make_plan(int ng, const dion3_group* g, const int* k, const dion3_ns
   return true;
 }
 
-// The side stream (default priority, not synchronising with the null stream)
-// and an event pool, created on a device's first step and kept until the
-// process ends.  Enqueueing a step holds the mutex, so concurrent callers do
-// not interleave their use of the events.
+// The library streams (default priority, not synchronising with the null
+// stream) and an event pool, created on a device's first step and kept until
+// the process ends.  Enqueueing a step holds the mutex, so concurrent callers
+// do not interleave their use of the events.
 struct SideCtx {
-  hipStream_t side = nullptr;
+  hipStream_t side = nullptr;   // gathers + Newton-Schulz, every compute unit
+  hipStream_t mem = nullptr;    // overlapped HBM-bound passes, half the compute units
   std::vector<hipEvent_t> ev;
 };
 constexpr int kMaxDevices = 64;
 static std::mutex g_side_mu;
 static SideCtx g_side[kMaxDevices];
+
+// Compute-unit mask of the overlapped stream: unit i is used when
+// (i mod 8 + i div 8) mod 8 < 4, which takes half of the units of every XCD
+// whether the units are numbered XCD by XCD or interleaved across XCDs.
+static int make_mem_stream(int dev, hipStream_t* out) {
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 16)
+    return hipStreamCreateWithFlags(out, hipStreamNonBlocking) == hipSuccess ? DION3_OK : DION3_ERR_HIP;
+  std::vector<uint32_t> mask((cus + 31) / 32, 0u);
+  for (int i = 0; i < cus; ++i)
+    if ((i % 8 + i / 8) % 8 < 4) mask[i / 32] |= 1u << (i % 32);
+  return hipExtStreamCreateWithCUMask(out, (uint32_t)mask.size(), mask.data()) == hipSuccess ? DION3_OK
+                                                                                           : DION3_ERR_HIP;
+}
 
 static int side_ctx(size_t nev, SideCtx** out) {
   int dev = 0;
@@ -77,6 +95,10 @@ static int side_ctx(size_t nev, SideCtx** out) {
   SideCtx& c = g_side[dev];
   if (!c.side && hipStreamCreateWithFlags(&c.side, hipStreamNonBlocking) != hipSuccess) {
     c.side = nullptr;
+    return DION3_ERR_HIP;
+  }
+  if (!c.mem && make_mem_stream(dev, &c.mem) != DION3_OK) {
+    c.mem = nullptr;
     return DION3_ERR_HIP;
   }
   while (c.ev.size() < nev) {
@@ -122,17 +144,30 @@ static int run_step(int n_groups, const dion3_group* groups, void* const* W, voi
 
   std::lock_guard<std::mutex> lock(g_side_mu);
   SideCtx* ctx = nullptr;
-  int st = side_ctx(3 * (size_t)nc + 1, &ctx);
+  int st = side_ctx(3 * (size_t)nc + 3, &ctx);
   if (st) return st;
-  hipStream_t side = ctx->side;
-  hipEvent_t* ev_sel = ctx->ev.data();          // class c selected (caller's stream)
+  hipStream_t side = ctx->side, mem = ctx->mem;
+  hipEvent_t* ev_sel = ctx->ev.data();          // class c selected
   hipEvent_t* ev_ns = ev_sel + nc;              // class c orthogonalised (side stream)
-  hipEvent_t* ev_upd = ev_ns + nc;              // class c updated (caller's stream)
-  hipEvent_t ev_end = ev_upd[nc];               // side stream drained
+  hipEvent_t* ev_upd = ev_ns + nc;              // class c updated
+  hipEvent_t ev_fork = ev_upd[nc];              // first class selected (caller's stream)
+  hipEvent_t ev_side_end = ev_upd[nc + 1];      // side stream drained
+  hipEvent_t ev_mem_end = ev_upd[nc + 2];       // overlapped stream drained
   auto hip_ok = [](hipError_t e) { return e == hipSuccess ? DION3_OK : DION3_ERR_HIP; };
+  // class c's momentum pass: the caller's stream for the first class, else the
+  // overlapped stream; class c's update: the caller's stream for the last
+  auto sel_stream = [&](int c) { return c == 0 ? s : mem; };
+  auto upd_stream = [&](int c) { return c == nc - 1 ? s : mem; };
 
-  // caller's stream: momentum + selection of every group, class by class
+  bool used_side = false, used_mem = false;
   for (int c = 0; c < nc && !st; ++c) {
+    hipStream_t sc = sel_stream(c);
+    if (c == 1) {
+      st = hip_ok(hipEventRecord(ev_fork, s));
+      if (!st) st = hip_ok(hipStreamWaitEvent(mem, ev_fork, 0));
+      used_mem = used_mem || !st;
+      if (st) break;
+    }
     for (int i : P.classes[c]) {
       const dion3_group& gi = groups[i];
       // deferred error feedback: idx[i] holds the previous selection on entry;
@@ -140,20 +175,19 @@ static int run_step(int n_groups, const dion3_group* groups, void* const* W, voi
       st = dion3_momentum_rowsel_ef(&gi, M[i], G[i], k[i], idx[i], nullptr,
                                     (double*)(sqn_base + P.sqn_off[i]),
                                     deferred && has_prev ? idx[i] : nullptr, k[i], mu, rs_ws,
-                                    P.rowsel, s);
+                                    P.rowsel, sc);
       if (st) break;
     }
-    if (!st) st = hip_ok(hipEventRecord(ev_sel[c], s));
+    if (!st) st = hip_ok(hipEventRecord(ev_sel[c], sc));
   }
-  // per class: gather + Newton-Schulz on the side stream, update on the caller's
-  bool forked = false;
+  // per class: gather + Newton-Schulz on the side stream, then the update
   for (int c = 0; c < nc && !st; ++c) {
     const auto& cls = P.classes[c];
     const int kk = k[cls[0]], mm = P.m[cls[0]];
     const size_t slice = (size_t)kk * mm * es;
     char* O = Obuf[c & 1];
     st = hip_ok(hipStreamWaitEvent(side, ev_sel[c], 0));
-    forked = forked || !st;
+    used_side = used_side || !st;
     // O is rewritten two classes later: wait until that class's update read it
     if (!st && c >= 2) st = hip_ok(hipStreamWaitEvent(side, ev_upd[c - 2], 0));
     int nb = 0;
@@ -166,24 +200,27 @@ static int run_step(int n_groups, const dion3_group* groups, void* const* W, voi
     }
     if (!st) st = dion3_gram_ns(nb, kk, mm, p, X0, O, gws, P.gram, side);
     if (!st) st = hip_ok(hipEventRecord(ev_ns[c], side));
-    if (!st) st = hip_ok(hipStreamWaitEvent(s, ev_ns[c], 0));
+    hipStream_t uc = upd_stream(c);
+    if (!st) st = hip_ok(hipStreamWaitEvent(uc, ev_ns[c], 0));
     nb = 0;
     for (int i : cls) {
       if (st) break;
       const dion3_group& gi = groups[i];
       st = dion3_apply_rows(&gi, W[i], deferred ? nullptr : M[i], idx[i], kk, O + nb * slice, p->ns_dtype,
-                            (long long)kk * mm, eta, wd, mu, s);
+                            (long long)kk * mm, eta, wd, mu, uc);
       nb += gi.batch;
     }
-    if (!st) st = hip_ok(hipEventRecord(ev_upd[c], s));
+    if (!st) st = hip_ok(hipEventRecord(ev_upd[c], uc));
   }
-  // join: the caller's stream waits for everything enqueued on the side stream
-  // (also after an error, so that no side-stream work outlives the call's order)
-  if (forked) {
-    const int j = hip_ok(hipEventRecord(ev_end, side));
-    const int w = j ? j : hip_ok(hipStreamWaitEvent(s, ev_end, 0));
+  // join: the caller's stream waits for everything enqueued on the library
+  // streams (also after an error, so that no such work escapes the call's order)
+  auto join = [&](hipStream_t from, hipEvent_t e) {
+    const int j = hip_ok(hipEventRecord(e, from));
+    const int w = j ? j : hip_ok(hipStreamWaitEvent(s, e, 0));
     if (!st) st = w;
-  }
+  };
+  if (used_side) join(side, ev_side_end);
+  if (used_mem) join(mem, ev_mem_end);
   return st;
 }
 
