@@ -32,6 +32,11 @@ template <> struct Mma<f16> {
     acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a),
                                                  __builtin_bit_cast(half8, b), acc, 0, 0, 0);
   }
+  // acc = a b (the accumulator input is zero)
+  __device__ static void first(floatx16& acc, const uint4& a, const uint4& b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a),
+                                                 __builtin_bit_cast(half8, b), floatx16{}, 0, 0, 0);
+  }
 };
 
 template <> struct Mma<bf16_t> {
@@ -39,6 +44,10 @@ template <> struct Mma<bf16_t> {
   __device__ static void run(floatx16& acc, const uint4& a, const uint4& b) {
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bfx8, a),
                                                   __builtin_bit_cast(bfx8, b), acc, 0, 0, 0);
+  }
+  __device__ static void first(floatx16& acc, const uint4& a, const uint4& b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bfx8, a),
+                                                  __builtin_bit_cast(bfx8, b), floatx16{}, 0, 0, 0);
   }
 };
 
@@ -68,6 +77,8 @@ struct KParams {
   void* C; long long ldc, sC;
   float alpha, beta, gamma;
   int tiles_m, tiles_n, tiles_per_mat;
+  int ntiles;          // tiles over the batch
+  int tiles_per_wg;    // large-tile kernel: tiles run back to back by one work-group
 };
 
 // LDS position of 16-byte chunk `chunk` of tile row `row`.  A 128-bit LDS read
@@ -280,44 +291,31 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(KParams p) {
 // ---------------------------------------------------------------------------
 // Large-tile kernel for fp16 / bf16: a 256 x 256 tile per work-group, 4 waves
 // in 2 x 2, each wave owning a 128 x 128 block (4 x 4 MFMA 32x32x16 tiles), so
-// every 16-byte fragment read from LDS feeds four MFMAs.  A stage holds 64 K
-// elements (128 bytes per row) of both operands, 64 KB; two stages live in LDS.
+// every 16-byte fragment read from LDS feeds four MFMAs.  A stage holds 32 K
+// elements of both operands (32 KB); NBUF stages rotate through LDS.
 //
-// K-contiguous operands travel from global memory straight into LDS with
-// buffer loads that write LDS directly (each lane's 16 bytes land at the
-// wave's LDS base + 16 x lane), so no registers are spent on staging: lane L of
-// a wave instruction covering rows r0..r0+7 fetches row r = r0 + L/8, the chunk
-// whose swizzled position is L mod 8, which puts every chunk in its place.
-// The N-contiguous B operand of Q X is instead loaded as 8 x 8 element blocks
-// into registers and transposed there, so LDS is always written with 16-byte
-// K-contiguous chunks.  MFMA fragments are double-buffered across k-steps so
-// LDS latency overlaps the MFMAs of the previous step.
+// Operands travel from global memory straight into LDS with buffer loads that
+// write LDS directly (each lane's 16 bytes land at the wave's LDS base + 16 x
+// lane), so no registers are spent on staging.  K-contiguous operands land as
+// 64-byte rows with a row-dependent chunk swizzle; the N-contiguous X of Q X
+// lands as 512-byte rows and its MFMA fragments come from transposing LDS
+// reads (ds_read_b64_tr_b16), which hand each lane four consecutive K values
+// of one column.  MFMA fragments are double-buffered across k-steps so LDS
+// latency overlaps the MFMAs of the previous step.
+//
+// Q X runs several tiles per work-group: the stage sequence continues from one
+// tile into the next, so the next tile's first stages are loaded while the
+// current tile finishes, and the MFMA computes C^T blocks (operands swapped),
+// which leaves four consecutive columns of one row in each lane; one lane swap
+// across the two half-waves then forms 16-byte row chunks, and a tile is
+// written with 32 stores per wave that stay in flight while the next tile
+// computes.
 // ---------------------------------------------------------------------------
 template <int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (N > 0) {
     static_for<N - 1>(f);
     f(std::integral_constant<int, N - 1>{});
-  }
-}
-
-template <typename T>
-__device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8]) {
-  // in[r] holds elements (r, 0..7); out[c] receives elements (0..7, c)
-  uint32_t w[8][4];
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    w[r][0] = in[r].x; w[r][1] = in[r].y; w[r][2] = in[r].z; w[r][3] = in[r].w;
-  }
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    uint32_t d[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t a = w[2 * q][c >> 1], b = w[2 * q + 1][c >> 1];
-      d[q] = (c & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-    }
-    out[c] = make_uint4(d[0], d[1], d[2], d[3]);
   }
 }
 
@@ -335,12 +333,12 @@ __device__ __forceinline__ int4v make_rsrc(const void* base, long long bytes) {
 }
 
 // One wave instruction: 64 lanes x 16 bytes from rsrc at voffset + soffset
-// into LDS at `lds` (wave-uniform) + 16 x lane.  Issued from inline assembly
-// so that the compiler does not wait for it before unrelated LDS reads: the
-// caller waits (vmcnt) before the barrier that publishes the stage.
-__device__ __forceinline__ void lds_dma16(const int4v& rsrc, const void* lds, int voffset, int soffset) {
-  const int m0 = __builtin_amdgcn_readfirstlane((int)(unsigned)(uintptr_t)
-      (const __attribute__((address_space(3))) void*)lds);
+// into LDS at byte address `lds` (wave-uniform) + 16 x lane.  Issued from
+// inline assembly so that the compiler does not wait for it before unrelated
+// LDS reads: the caller waits (vmcnt) before the barrier that publishes the
+// stage.
+__device__ __forceinline__ void lds_dma16(const int4v& rsrc, unsigned lds, int voffset, int soffset) {
+  const int m0 = __builtin_amdgcn_readfirstlane((int)lds);
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :: "s"(m0), "v"(voffset), "s"(rsrc), "s"(soffset) : "memory", "m0");
 }
@@ -361,27 +359,62 @@ __device__ __forceinline__ int swzn(int kr, int n) {
   return kr * 512 + ((((n >> 3) ^ (2 * (kr & 3)))) << 4) + ((n & 4) << 1);
 }
 
-__device__ __forceinline__ void wait_vm_stages(int n) {   // n: DMA stages allowed in flight
-  if (n <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else if (n == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else if (n == 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+// Wait until at most n vector memory operations of this wave are outstanding
+// (n: a multiple of 8 up to 56; 8 DMA instructions per stage, 32 stores per
+// tile epilogue).  The counter retires loads and stores in issue order.
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 16: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+    case 24: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+    case 32: asm volatile("s_waitcnt vmcnt(32)" ::: "memory"); break;
+    case 40: asm volatile("s_waitcnt vmcnt(40)" ::: "memory"); break;
+    case 48: asm volatile("s_waitcnt vmcnt(48)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
 }
 
 typedef short short4v __attribute__((ext_vector_type(4)));
 
-// Large-tile kernel (fp16 / bf16, whole tiles only).  Stage s of the K loop
-// (32 K elements of both operands, 32 KB) lives in LDS buffer s mod NBUF.  Its
-// loads are issued right after the barrier that ends stage s - NBUF (the last
+// Read one accumulator out of its AGPR where it is used (an inline read keeps
+// the register allocator from copying every accumulator to VGPRs at once).
+__device__ __forceinline__ float acc_read(float v) {
+  float r;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(v));
+  return r;
+}
+
+struct TileAddr {
+  int4v ra, rb;      // buffer resources based at the tile's first A row / B row or column
+  int m0, n0, bat, ti, tj;
+};
+
+constexpr int kEpiStores = 32;   // 16-byte stores per wave in a Q X tile epilogue
+
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v* lds_s4_ptr;
+
+// 16-byte LDS read at byte address `addr`
+__device__ __forceinline__ uint4 lds_read16(unsigned addr) {
+  const u32x4v v = *(const __attribute__((address_space(3))) u32x4v*)(uintptr_t)addr;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Large-tile kernel (fp16 / bf16, whole tiles only).  Global stage g (stage g
+// mod KT of the work-group's tile g / KT) lives in LDS buffer g mod NBUF.  Its
+// loads are issued right after the barrier that ends stage g - NBUF (the last
 // use of that buffer) and must have landed by the barrier that ends stage
-// s - 2; the first k-step's fragments of stage s are then read during stage
-// s - 1, so a wave leaves every barrier with its next MFMA operands in
+// g - 2; the first k-step's fragments of stage g are then read during stage
+// g - 1, so a wave leaves every barrier with its next MFMA operands in
 // registers.  Each wave issues 8 one-kilobyte DMA instructions per stage.
 template <typename T, typename TO, int OP, int NBUF>
 __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm256_kernel(KParams p) {
   constexpr bool SYM = OP != OP_GEMM;
   constexpr bool BT = OP == OP_GEMM;
+  constexpr bool SWAP = OP == OP_GEMM;              // MFMA produces C^T blocks
+  constexpr bool MULTI = SWAP && sizeof(TO) == 2;   // several tiles per work-group
   constexpr int BM = 256, BN = 256;
   constexpr int BK = 32;                      // K elements per stage
   constexpr int WT = 128;                     // wave tile edge
@@ -389,59 +422,67 @@ void gemm256_kernel(KParams p) {
   constexpr int STAGE = 32768;                // bytes per stage (both operands)
 
   __shared__ __attribute__((aligned(1024))) char smem[NBUF * STAGE];
+  const unsigned lds0 = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)smem;
 
+  // XCD-aware order: consecutive ids run on one XCD at the same time
   const int G = gridDim.x;
   const int wg = blockIdx.x;
   const int per = G / 8;
   const int id = wg < per * 8 ? (wg % 8) * per + wg / 8 : wg;
-  const int bat = id / p.tiles_per_mat;
-  const int t = id % p.tiles_per_mat;
-  int ti, tj;
-  if (SYM) {
-    tri_index(t, ti, tj);
-  } else {
-    ti = t % p.tiles_m;
-    tj = t / p.tiles_m;
-  }
-  // the tile coordinates are uniform: keep them (and the buffer resources
-  // derived from them) in scalar registers
-  ti = __builtin_amdgcn_readfirstlane(ti);
-  tj = __builtin_amdgcn_readfirstlane(tj);
-  const int bu = __builtin_amdgcn_readfirstlane(bat);
-  const int m0 = ti * BM, n0 = tj * BN;
-
-  const T* A = (const T*)p.A + bu * p.sA;
-  const T* B = (const T*)p.B + bu * p.sB;
+  // this work-group's tiles: id, id + G, ... (fewer at the end of the range)
+  const int nt = MULTI ? min(p.tiles_per_wg, (p.ntiles - id + G - 1) / G) : 1;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar LDS offsets
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- DMA addressing.  K-contiguous operand: wave instruction s (0..3)
-  // covers tile rows 64 s + 16 wave + [0, 16); lane L fetches row
-  // 64 s + 16 wave + L/4 and the chunk whose swizzled position is L mod 4.
-  const int4v ra = make_rsrc(A, (long long)p.M * p.lda * 2);
-  const int va = ((m0 + 16 * wave + (lane >> 2)) * (int)p.lda + (((lane & 3) ^ (lane >> 4)) << 3)) * 2;
+  // ---- DMA addressing (per-lane offsets from the tile's buffer base).
+  // K-contiguous operand: wave instruction q (0..3) covers tile rows
+  // 64 q + 16 wave + [0, 16); lane L fetches row 64 q + 16 wave + L/4 and the
+  // chunk whose swizzled position is L mod 4.  N-contiguous B (Q X):
+  // instruction q covers stage rows 8 q + 2 wave + {0, 1}; lane L fetches row
+  // 8 q + 2 wave + L/32, the chunk whose swizzled position is L mod 32.
+  const int va = ((16 * wave + (lane >> 2)) * (int)p.lda + (((lane & 3) ^ (lane >> 4)) << 3)) * 2;
   const int ka = 64 * (int)p.lda * 2;                 // +64 rows per instruction
-  // B operand: K-contiguous (symmetric products) like A, or N-contiguous (Q X):
-  // instruction s covers stage rows 8 s + 2 wave + {0, 1}; lane L fetches
-  // row 8 s + 2 wave + L/32, the chunk whose swizzled position is L mod 32
-  const int4v rb = make_rsrc(B, BT ? (long long)p.K * p.ldb * 2 : (long long)p.N * p.ldb * 2);
   int vb, kb;
   if (!BT) {
-    vb = ((n0 + 16 * wave + (lane >> 2)) * (int)p.ldb + (((lane & 3) ^ (lane >> 4)) << 3)) * 2;
+    vb = ((16 * wave + (lane >> 2)) * (int)p.ldb + (((lane & 3) ^ (lane >> 4)) << 3)) * 2;
     kb = 64 * (int)p.ldb * 2;
   } else {
     const int kr = 2 * wave + (lane >> 5);
-    vb = (kr * (int)p.ldb + n0 + (((lane & 31) ^ (2 * (kr & 3))) << 3)) * 2;
+    vb = (kr * (int)p.ldb + (((lane & 31) ^ (2 * (kr & 3))) << 3)) * 2;
     kb = 8 * (int)p.ldb * 2;                          // +8 rows per instruction
   }
+  auto tile_addr = [&](int L, TileAddr& a) {
+    int bat = L / p.tiles_per_mat;
+    const int t = L - bat * p.tiles_per_mat;
+    int ti, tj;
+    if (SYM) {
+      tri_index(t, ti, tj);
+    } else {
+      ti = t % p.tiles_m;
+      tj = t / p.tiles_m;
+    }
+    // the tile coordinates are uniform: keep them (and the buffer resources
+    // derived from them) in scalar registers
+    a.ti = __builtin_amdgcn_readfirstlane(ti);
+    a.tj = __builtin_amdgcn_readfirstlane(tj);
+    a.bat = __builtin_amdgcn_readfirstlane(bat);
+    a.m0 = a.ti * BM;
+    a.n0 = a.tj * BN;
+    const T* A = (const T*)p.A + a.bat * p.sA + (long long)a.m0 * p.lda;
+    const T* B = (const T*)p.B + a.bat * p.sB + (BT ? (long long)a.n0 : (long long)a.n0 * p.ldb);
+    a.ra = make_rsrc(A, (long long)(p.M - a.m0) * p.lda * 2);
+    a.rb = make_rsrc(B, BT ? (long long)p.K * p.ldb * 2 - (long long)a.n0 * 2
+                           : (long long)(p.N - a.n0) * p.ldb * 2);
+  };
 
-  // one DMA instruction x (0..3: operand A, 4..7: operand B) of stage s
-  auto dma = [&](int s, int x) {
-    char* buf = smem + (s % NBUF) * STAGE;
-    const int k0 = s * BK;
+  // one DMA instruction x (0..3: operand A, 4..7: operand B) of the tile's
+  // stage ls into LDS buffer b
+  auto dma = [&](const int4v& ra, const int4v& rb, int ls, int b, int x) {
+    const unsigned buf = lds0 + (unsigned)(b * STAGE);
+    const int k0 = ls * BK;
     const int q = x & 3;
     if (x < 4) {
       lds_dma16(ra, buf + (64 * q + 16 * wave) * 64, va, k0 * 2 + q * ka);
@@ -451,49 +492,95 @@ void gemm256_kernel(KParams p) {
       lds_dma16(rb, buf + 16384 + (8 * q + 2 * wave) * 512, vb, k0 * (int)p.ldb * 2 + q * kb);
     }
   };
-  auto issue_stage = [&](int s) {
-#pragma unroll
-    for (int x = 0; x < 8; ++x) dma(s, x);
-  };
 
-  // fragments of one k-step (16 K elements): A rows wm*128 + 32 i + lane%32;
-  // B either likewise (K-contiguous) or through transposing reads (Q X)
-  auto read_a = [&](uint4& f, int s, int st, int i) {
-    const char* buf = smem + (s % NBUF) * STAGE;
-    f = *(const uint4*)(buf + swz32(wm * WT + i * 32 + (lane & 31), 2 * st + (lane >> 5)));
+  // fragments of one k-step (16 K elements) of global stage g: A rows
+  // wm*128 + 32 i + lane%32; B either likewise (K-contiguous) or through
+  // transposing reads (Q X)
+  auto read_a = [&](uint4& f, int g, int st, int i) {
+    const unsigned buf = lds0 + (unsigned)((g % NBUF) * STAGE);
+    f = lds_read16(buf + swz32(wm * WT + i * 32 + (lane & 31), 2 * st + (lane >> 5)));
   };
-  auto read_b = [&](uint4& f, int s, int st, int j) {
-    const char* buf = smem + (s % NBUF) * STAGE + 16384;
+  auto read_b = [&](uint4& f, int g, int st, int j) {
+    const unsigned buf = lds0 + (unsigned)((g % NBUF) * STAGE) + 16384;
     if (!BT) {
-      f = *(const uint4*)(buf + swz32(wn * WT + j * 32 + (lane & 31), 2 * st + (lane >> 5)));
+      f = lds_read16(buf + swz32(wn * WT + j * 32 + (lane & 31), 2 * st + (lane >> 5)));
     } else {
       // lane = 16 g + 4 q + t addresses row 16 st + 8 (g/2) + 4 h + q and
       // columns 16 (g mod 2) + 4 t .. +3 of the fragment's 32; the transposing
       // read hands each lane its column's four consecutive K values
-      const int g = lane >> 4, q = (lane >> 2) & 3, tt = lane & 3;
-      const int n = wn * WT + j * 32 + 16 * (g & 1) + 4 * tt;
-      const int kr0 = 16 * st + 8 * (g >> 1) + q;
-      const short4v h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) short4v*)(__attribute__((address_space(3))) char*)(buf + swzn(kr0, n)));
-      const short4v h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) short4v*)(__attribute__((address_space(3))) char*)(buf + swzn(kr0 + 4, n)));
+      const int gg = lane >> 4, q = (lane >> 2) & 3, tt = lane & 3;
+      const int n = wn * WT + j * 32 + 16 * (gg & 1) + 4 * tt;
+      const int kr0 = 16 * st + 8 * (gg >> 1) + q;
+      const short4v h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(uintptr_t)(buf + swzn(kr0, n)));
+      const short4v h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(uintptr_t)(buf + swzn(kr0 + 4, n)));
       f = make_uint4(__builtin_bit_cast(uint2, h0).x, __builtin_bit_cast(uint2, h0).y,
                      __builtin_bit_cast(uint2, h1).x, __builtin_bit_cast(uint2, h1).y);
     }
   };
 
+  // accumulators: the first k-step of every tile overwrites them (MFMA with a
+  // zero accumulator input), so they are dead between a tile's epilogue and
+  // the next tile
   floatx16 acc[SUB][SUB];
-#pragma unroll
-  for (int i = 0; i < SUB; ++i)
-#pragma unroll
-    for (int j = 0; j < SUB; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // Q X epilogue: block (i, j) of the wave holds C[row lane%32][8 g + 4 (lane/32)
+  // + 0..3] in acc[i][j][4 g .. 4 g + 3]; a lane swap across the half-waves gives
+  // lane L < 32 columns 16 h .. +7 and lane L + 32 columns 16 h + 8 .. +15
+  auto epilogue_swap = [&](const TileAddr& a) {
+    if constexpr (SWAP) {
+      TO* C = (TO*)p.C + a.bat * p.sC;
+      const int lc = lane & 31, lh = lane >> 5;
+      TO* rowp = C + (long long)(a.m0 + wm * WT + lc) * p.ldc + (a.n0 + wn * WT);
+      static_for<SUB>([&](auto ic) {
+        static_for<SUB>([&](auto jc) {
+          constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
+          // one block at a time: keeps the scheduler from moving every
+          // accumulator into vector registers at once
+          __builtin_amdgcn_sched_barrier(0);
+          TO* dst = rowp + (long long)(32 * i) * p.ldc + 32 * j;
+          if constexpr (sizeof(TO) == 2) {
+            uint32_t d[4][2];
+            static_for<4>([&](auto gc) {
+              constexpr int g = decltype(gc)::value;
+              static_for<2>([&](auto hc) {
+                constexpr int h = decltype(hc)::value;
+                const TO lo = Store<TO>::from_f32(p.alpha * acc_read(acc[i][j][4 * g + 2 * h]));
+                const TO hi = Store<TO>::from_f32(p.alpha * acc_read(acc[i][j][4 * g + 2 * h + 1]));
+                d[g][h] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+              });
+            });
+            static_for<2>([&](auto pc) {
+              constexpr int pr = decltype(pc)::value;
+              const auto s0 = __builtin_amdgcn_permlane32_swap(d[2 * pr][0], d[2 * pr + 1][0], false, false);
+              const auto s1 = __builtin_amdgcn_permlane32_swap(d[2 * pr][1], d[2 * pr + 1][1], false, false);
+              *(uint4*)(dst + 16 * pr + 8 * lh) = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+            });
+          } else {
+            static_for<4>([&](auto gc) {
+              constexpr int g = decltype(gc)::value;
+              *(float4*)(dst + 8 * g + 4 * lh) =
+                  make_float4(p.alpha * acc_read(acc[i][j][4 * g]), p.alpha * acc_read(acc[i][j][4 * g + 1]),
+                              p.alpha * acc_read(acc[i][j][4 * g + 2]), p.alpha * acc_read(acc[i][j][4 * g + 3]));
+            });
+          }
+        });
+      });
+    }
+  };
+
+  TileAddr cur, nxt;
+  tile_addr(id, cur);
+  if (MULTI && nt > 1) tile_addr(id + G, nxt);
+  else nxt = cur;
   const int KT = p.K / BK;
-  const int pre = KT < NBUF - 1 ? KT : NBUF - 1;
-  for (int s = 0; s < pre; ++s) issue_stage(s);
-  wait_vm_stages(pre - (KT < 2 ? KT : 2));            // stages 0 and 1 landed
+  const int GT = nt * KT;                     // stages over all tiles (KT >= NBUF when nt > 1)
+
+  const int pre = GT < NBUF - 1 ? GT : NBUF - 1;
+  for (int g = 0; g < pre; ++g)
+#pragma unroll
+    for (int x = 0; x < 8; ++x) dma(cur.ra, cur.rb, g, g, x);
+  wait_vm(8 * (pre - (GT < 2 ? GT : 2)));     // stages 0 and 1 landed
   __syncthreads();
 
   uint4 fa0[SUB], fb0[SUB], fa1[SUB], fb1[SUB];
@@ -504,46 +591,96 @@ void gemm256_kernel(KParams p) {
   // issues one DMA instruction of the stage NBUF - 1 ahead (spread out so
   // the vector memory queue never stalls the wave), then reads two fragments
   // of the next k-step (B fragments first), then runs its 4 MFMAs.
-  for (int kt = 0; kt < KT; ++kt) {
-    const bool iss = kt + NBUF - 1 < KT;
+  int g = 0;                                  // global stage
+  // FIRST: a tile's first stage (its first k-step starts the accumulators);
+  // LAST: a tile's last stage, which leaves the next stage's fragments unread
+  // so that the epilogue runs with them dead (they are read after it)
+  auto stage = [&](auto first_c, auto last_c, int j, int kt) {
+    constexpr bool FIRST = decltype(first_c)::value;
+    constexpr bool LAST = decltype(last_c)::value;
+    // the stage NBUF - 1 ahead: this tile's, or the next tile's first ones
+    const bool to_next = MULTI && kt + NBUF - 1 >= KT;
+    const bool iss = g + NBUF - 1 < GT;
+    const int ls = kt + NBUF - 1 >= KT ? kt + NBUF - 1 - KT : kt + NBUF - 1;
+    const int ib = (g + NBUF - 1) % NBUF;
+    int4v ira = cur.ra, irb = cur.rb;
+    if (to_next) { ira = nxt.ra; irb = nxt.rb; }
     static_for<2 * SUB>([&](auto gxc) {
       constexpr int gx = decltype(gxc)::value;
       constexpr int st = gx / SUB, x = gx % SUB;     // k-step, MFMA row block
       __builtin_amdgcn_sched_barrier(0);
-      if (iss) dma(kt + NBUF - 1, gx);
+      if (iss) dma(ira, irb, ls, ib, gx);
       // next k-step: step 1 of this stage, or step 0 of the next stage
-      const int ns = st == 0 ? kt : kt + 1;
-      const int nst = st == 0 ? 1 : 0;
-      uint4 (&na)[SUB] = st == 0 ? fa1 : fa0;
-      uint4 (&nb)[SUB] = st == 0 ? fb1 : fb0;
-      if (x < 2) {
-        read_b(nb[2 * x], ns, nst, 2 * x);
-        read_b(nb[2 * x + 1], ns, nst, 2 * x + 1);
-      } else {
-        read_a(na[2 * x - 4], ns, nst, 2 * x - 4);
-        read_a(na[2 * x - 3], ns, nst, 2 * x - 3);
+      if (!(LAST && st == 1)) {
+        const int ns = st == 0 ? g : g + 1;
+        const int nst = st == 0 ? 1 : 0;
+        uint4 (&na)[SUB] = st == 0 ? fa1 : fa0;
+        uint4 (&nb)[SUB] = st == 0 ? fb1 : fb0;
+        if (x < 2) {
+          read_b(nb[2 * x], ns, nst, 2 * x);
+          read_b(nb[2 * x + 1], ns, nst, 2 * x + 1);
+        } else {
+          read_a(na[2 * x - 4], ns, nst, 2 * x - 4);
+          read_a(na[2 * x - 3], ns, nst, 2 * x - 3);
+        }
       }
       uint4 (&ca)[SUB] = st == 0 ? fa0 : fa1;
       uint4 (&cbv)[SUB] = st == 0 ? fb0 : fb1;
 #pragma unroll
-      for (int j = 0; j < SUB; ++j) Mma<T>::run(acc[x][j], ca[x], cbv[j]);
+      for (int jj = 0; jj < SUB; ++jj) {
+        const uint4& l = SWAP ? cbv[jj] : ca[x];
+        const uint4& r = SWAP ? ca[x] : cbv[jj];
+        if (FIRST && st == 0) Mma<T>::first(acc[x][jj], l, r);
+        else Mma<T>::run(acc[x][jj], l, r);
+      }
     });
     __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < KT) {
-      // stage kt + 2 must land before this barrier; later stages may fly on
-      const int last_issued = kt + NBUF - 1 < KT ? kt + NBUF - 1 : KT - 1;
-      wait_vm_stages(kt + 2 < KT ? last_issued - (kt + 2) : 0);
+    if (g + 1 < GT) {
+      // stage g + 2 must land before this barrier; later stages may fly on,
+      // and so may the previous tile's epilogue stores when they were issued
+      // after stage g + 2's loads (the first two stages of a tile)
+      const int last_issued = g + NBUF - 1 < GT ? g + NBUF - 1 : GT - 1;
+      int allowed = g + 2 < GT ? 8 * (last_issued - (g + 2)) : 0;
+      if (MULTI && g + 2 < GT && j > 0 && kt < 2) allowed += kEpiStores;
+      wait_vm(allowed);
       __syncthreads();
+    }
+    ++g;
+  };
+  using T1 = std::true_type;
+  using T0 = std::false_type;
+  for (int j = 0; j < nt; ++j) {
+    stage(T1{}, T0{}, j, 0);
+    for (int kt = 1; kt < KT; ++kt) stage(T0{}, T0{}, j, kt);
+    if constexpr (MULTI) {
+      // the finished tile's stores stay in flight while the next tile, whose
+      // first stages are already loaded, computes
+      epilogue_swap(cur);
+      // the next tile's first fragments (after the last tile: an in-bounds
+      // read of a buffer no load is writing, unused)
+#pragma unroll
+      for (int i = 0; i < SUB; ++i) { read_a(fa0[i], g, 0, i); read_b(fb0[i], g, 0, i); }
+      if (j + 1 < nt) {
+        cur = nxt;
+        if (j + 2 < nt) tile_addr(id + (j + 2) * G, nxt);
+      }
     }
   }
 
-  // ---- epilogue.  Direct tile: each lane stores its values at C[gi][gj].
-  // Mirror (symmetric ops): the values are also written transposed into LDS,
-  // then copied out as whole 512-byte rows to C[gj][gi]; on diagonal tiles
-  // only the strict upper part is copied, so every entry is written once.
-  TO* C = (TO*)p.C + bu * p.sC;
-  const TO* E = (const TO*)p.E + (p.E ? bu * p.sE : 0);
-  const bool diag_tile = SYM && ti == tj;
+  if constexpr (SWAP) {
+    if constexpr (!MULTI) epilogue_swap(cur);
+    return;
+  }
+
+  // ---- symmetric epilogue (one tile per work-group).  Direct tile: each
+  // lane stores its values at C[gi][gj].  Mirror: the values are also written
+  // transposed into LDS, then copied out as whole 512-byte rows to C[gj][gi];
+  // on diagonal tiles only the strict upper part is copied, so every entry is
+  // written once.
+  const int m0 = cur.m0, n0 = cur.n0;
+  TO* C = (TO*)p.C + cur.bat * p.sC;
+  const TO* E = (const TO*)p.E + (p.E ? cur.bat * p.sE : 0);
+  const bool diag_tile = SYM && cur.ti == cur.tj;
   const bool upper_wave = diag_tile && wm < wn;   // the mirror of the lower quadrant
   constexpr bool HAS_E = OP == OP_SQ_ADD || OP == OP_SYRK;
   const bool use_e = OP == OP_SQ_ADD || (OP == OP_SYRK && p.beta != 0.f);
@@ -654,6 +791,36 @@ void gemm256_kernel(KParams p) {
   }
 }
 
+// Tiles per work-group for the multi-tile Q X kernel.  A work-group pays the
+// first stages' load latency once and then runs its tiles back to back; with
+// T tiles per work-group the launch takes ceil(ceil(n / T) / CUs) rounds of
+// T tiles.  The choice minimises rounds x (T x tile + start-up), with a tile
+// costing about (KT + 1) stage times and the start-up about 6.
+static int compute_units() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+static long long multi_tile_grid(long long ntiles, int KT, int& per_wg) {
+  const long long cus = compute_units();
+  double best = 0.0;
+  per_wg = 1;
+  for (int t = 1; t <= 8; ++t) {
+    const long long wgs = (ntiles + t - 1) / t;
+    const long long rounds = (wgs + cus - 1) / cus;
+    const double cost = (double)rounds * ((double)t * (KT + 1) + 6.0);
+    if (t == 1 || cost < best) { best = cost; per_wg = t; }
+  }
+  return (ntiles + per_wg - 1) / per_wg;
+}
+
 template <typename T, typename TO, int OP, int BM>
 static int launch_typed(const GemmArgs& a, hipStream_t s) {
   constexpr int BKE = kRowBytes / (int)sizeof(T);
@@ -692,12 +859,18 @@ static int launch_typed(const GemmArgs& a, hipStream_t s) {
   p.tiles_n = tn;
   p.tiles_per_mat = OP == OP_GEMM ? tm * tn : tm * (tm + 1) / 2;
   if (grid <= 0 || grid > 0x7fffffffLL) return DION3_ERR_UNSUPPORTED;
+  p.ntiles = (int)grid;
+  p.tiles_per_wg = 1;
+  long long wgs = grid;
+  if constexpr (OP == OP_GEMM && sizeof(TO) == 2) {
+    if (big && a.K / 32 >= kStages) wgs = multi_tile_grid(grid, a.K / 32, p.tiles_per_wg);
+  }
 
   static const char* names[4] = {"syrk", "sym_sq_add", "sym_mul", "gemm_qx"};
   TimedLaunch tl(names[OP], s);
   if (big) {
     if constexpr (HALF)
-      hipLaunchKernelGGL((gemm256_kernel<T, TO, OP, kStages>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL((gemm256_kernel<T, TO, OP, kStages>), dim3((unsigned)wgs), dim3(kThreads), 0, s, p);
   } else if (fast_for(BM))
     hipLaunchKernelGGL((gemm_kernel<T, TO, OP, false, BM>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
   else
