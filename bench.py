@@ -174,15 +174,19 @@ def run_step_bench(d, synth, torch, args):
 
     launches_per_step = 64
     d.dion3_timing_enable(launches_per_step * args.steps + 64)
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    # one event between consecutive steps: the mean over the timed region and
+    # the per-step median / 90th percentile
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        plan.step_deferred(eta, 0.0, MU, has_prev=args.warmup > 0 or _ > 0)
-    end.record()
+    ev[0].record()
+    for i in range(args.steps):
+        plan.step_deferred(eta, 0.0, MU, has_prev=args.warmup > 0 or i > 0)
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    pct = {"p50": per_step[len(per_step) // 2],
+           "p90": per_step[min(len(per_step) - 1, int(math.ceil(0.9 * len(per_step))) - 1)]}
     per_kernel = d.dion3_timing_report()
     d.dion3_timing_enable(0)
     print(f"# timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
@@ -206,7 +210,7 @@ def run_step_bench(d, synth, torch, args):
                        "achieved": round(ach, 2), "unit": unit, "frac": round(ach / peak, 4)}
     del plan, Ws, Ms, Gs, idxs
     torch.cuda.empty_cache()
-    return ms, table, groups, ks, eta
+    return ms, pct, table, groups, ks, eta
 
 
 def run_microbench(d, synth, torch):
@@ -266,7 +270,7 @@ def main():
         print(f"# copy reference: {args.copy_ref_mib} MiB read + written", file=sys.stderr, flush=True)
         del src, dst
 
-    ms, table, groups, ks, eta = run_step_bench(d, synth, torch, args)
+    ms, pct, table, groups, ks, eta = run_step_bench(d, synth, torch, args)
     micro = [] if args.no_microbench else run_microbench(d, synth, torch)
     if micro:
         print("# microbench done", file=sys.stderr, flush=True)
@@ -288,9 +292,11 @@ def main():
         "metric": "optimizer step ms (7B shape set, f=1/4) + sym-GEMM TFLOP/s vs MFMA peak",
         "value": round(ms, 3), "unit": "ms", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": False,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 storage, f16 Newton-Schulz",
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "ms_per_step_p50": round(pct["p50"], 3), "ms_per_step_p90": round(pct["p90"], 3),
         "data": "synthetic (Gaussian gradients with log-normal line scales, seeded)",
         "config": {"workload": f"{args.set} shape set Dion3 step, f={args.f:g}",
+                   "storage": "bf16 W, M, G; f16 Newton-Schulz (fp32 accumulation)",
                    "groups": [list(g) for g in groups], "k": ks, "T": 5, "restart_after": 2,
                    "mu": MU, "eta": eta},
         "roofline": roof,
