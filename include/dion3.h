@@ -143,6 +143,17 @@ size_t dion3_gram_ns_workspace_bytes(int batch, int k, int m, int ns_dtype);
 int dion3_gram_ns(int batch, int k, int m, const dion3_ns_params* p, const void* X0,
                   void* O, void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace bytes dion3_standard_ns needs. */
+size_t dion3_standard_ns_workspace_bytes(int batch, int k, int m, int ns_dtype);
+
+/* Standard Newton-Schulz on the symmetric kernels (Section 2 for the
+ * iteration; Section 4 and Appendix C.3: the fall-back used when the aspect
+ * ratio m / k is 1).  Arguments as dion3_gram_ns; p->restart_mask is ignored.
+ * Per iteration t: A = X X^T, Z = a_t I + b_t A + c_t A^2, X <- Z X, i.e.
+ * X <- a_t X + (b_t A + c_t A^2) X with the a_t X term carried by Z. */
+int dion3_standard_ns(int batch, int k, int m, const dion3_ns_params* p, const void* X0,
+                      void* O, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------- symmetric building blocks
  * (Section 5: triangular tile schedule, mirrored write-back, diagonal tiles
  * written once.)  dtype: DION3_F16, DION3_BF16 or DION3_F32 for operands and
@@ -204,7 +215,8 @@ size_t dion3_step_workspace_bytes(int n_groups, const dion3_group* groups, const
  * Section 6, with Gram Newton-Schulz, Section 4).  For every group i:
  * dion3_momentum_rowsel, dion3_gather_rows; groups whose canonical (k, m)
  * agree are then orthogonalised in one batched dion3_gram_ns call (the pages'
- * megabatching of same-shape matrices, on one GPU); finally
+ * megabatching of same-shape matrices, on one GPU; dion3_standard_ns when
+ * k = m, the aspect-ratio-1 fall-back of Section 4); finally
  * dion3_apply_rows.  W[i], M[i], G[i] are the group tensors, idx[i] receives
  * the [batch][k[i]] selected indices.  eta, wd, mu as in dion3_apply_rows
  * (one value for all groups).
@@ -212,9 +224,12 @@ size_t dion3_step_workspace_bytes(int n_groups, const dion3_group* groups, const
  * enqueued on `stream`; the gathers and Newton-Schulz products run on a side
  * stream, and the other momentum passes and updates on a stream limited to
  * half of the compute units, so that they overlap another class's products.
- * Both library streams belong to the current device; the library creates them
+ * The library streams belong to the current device; the library creates them
  * (with an event pool) on the device's first step and keeps them until the
- * process ends.  Events order all three against `stream`: when the call
+ * process ends.  Graph capture is not supported: a call on a capturing stream
+ * returns DION3_ERR_UNSUPPORTED and enqueues nothing (a query of the capture
+ * state that fails, e.g. on the legacy null stream while another stream
+ * captures, returns DION3_ERR_HIP).  Events order all three against `stream`: when the call
  * returns, everything it enqueued is ordered before later work on `stream`,
  * as if all of it had been enqueued there; `stream` must belong to the
  * current device.  Concurrent calls on one device are serialised while they

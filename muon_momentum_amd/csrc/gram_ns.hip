@@ -184,3 +184,49 @@ extern "C" int dion3_gram_ns(int batch, int k, int m, const dion3_ns_params* p, 
   }
   return st;
 }
+
+// Standard Newton-Schulz on the same symmetric kernels ("Dion3: Full-Stack
+// Orthogonal Updates", Section 2 for the iteration; Section 4 and Appendix C.3
+// for the fall-back when the aspect ratio is 1).  Per iteration on X:
+//   A = X X^T                  (symmetric kernel, lower triangle + mirror)
+//   Z = a I + b A + c A^2      (A^2 + B kernel, the identity in its epilogue)
+//   X <- Z X                   (rectangular kernel)
+// which is X <- a X + (b A + c A^2) X with the a X term carried by Z.
+// Buffers: X0 read only; outputs alternate between a k x m workspace slice
+// and O so that the last iteration writes O; two k x k slices hold A and Z.
+extern "C" size_t dion3_standard_ns_workspace_bytes(int batch, int k, int m, int ns_dtype) {
+  if (batch < 1 || k < 1 || m < 1 || !ns_dtype_ok(ns_dtype)) return 0;
+  const size_t es = dtype_size(ns_dtype);
+  return align256((size_t)batch * k * m * es) + 2 * align256((size_t)batch * k * k * es);
+}
+
+extern "C" int dion3_standard_ns(int batch, int k, int m, const dion3_ns_params* p, const void* X0,
+                                 void* O, void* ws, size_t ws_bytes, void* stream) {
+  if (batch < 1 || k < 1 || m < 1 || k > m || !p || !X0 || !O || X0 == O) return DION3_ERR_INVALID_ARG;
+  if (p->T < 1 || !p->coeffs || !ns_dtype_ok(p->ns_dtype)) return DION3_ERR_INVALID_ARG;
+  for (int i = 0; i < 3 * p->T; ++i)
+    if (!(p->coeffs[i] == p->coeffs[i])) return DION3_ERR_INVALID_ARG;
+  const size_t need = dion3_standard_ns_workspace_bytes(batch, k, m, p->ns_dtype);
+  if (!ws || ws_bytes < need) return DION3_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const int dt = p->ns_dtype;
+  const size_t es = dtype_size(dt);
+  const long long skm = (long long)k * m, skk = (long long)k * k;
+  char* w = (char*)ws;
+  void* Xw = w;
+  void* A = w + align256((size_t)batch * skm * es);
+  void* Z = (char*)A + align256((size_t)batch * skk * es);
+  const void* cur = X0;
+  int st = DION3_OK;
+  for (int t = 0; t < p->T && st == DION3_OK; ++t) {
+    const float a = (float)p->coeffs[3 * t + 0];
+    const float b = (float)p->coeffs[3 * t + 1];
+    const float c = (float)p->coeffs[3 * t + 2];
+    void* out = ((p->T - 1 - t) % 2 == 0) ? O : Xw;
+    st = sym_op(OP_SYRK, batch, k, m, dt, cur, skm, cur, skm, nullptr, 0, A, skk, 1.f, 0.f, 0.f, s);
+    if (!st) st = sym_op(OP_SQ_ADD, batch, k, k, dt, A, skk, A, skk, A, skk, Z, skk, c, b, a, s);
+    if (!st) st = qx_op(batch, k, m, dt, Z, skk, cur, skm, dt, out, skm, 1.f, s);
+    cur = out;
+  }
+  return st;
+}

@@ -1,9 +1,11 @@
 // Whole-step driver: momentum + selection, gather, batched Gram Newton-Schulz
 // per canonical shape, and the fused update.
 //
-// Method: "Dion3: Full-Stack Orthogonal Updates", Section 6 (update rule) and
+// Method: "Dion3: Full-Stack Orthogonal Updates", Section 6 (update rule),
 // Section 7 (megabatching: every matrix of one shape is processed as one
-// batch).  On one GPU the batching is across launches: matrices whose selected
+// batch) and Section 4 (a class whose selected submatrices are square uses
+// standard Newton-Schulz on the symmetric kernels, Gram Newton-Schulz
+// otherwise).  On one GPU the batching is across launches: matrices whose selected
 // submatrices have the same (k, m) share one Newton-Schulz batch, so an
 // up-projection group (row selection) and a down-projection group (column
 // selection, stored transposed) run their Newton-Schulz together.
@@ -57,18 +59,20 @@ static bool make_plan(int ng, const dion3_group* g, const int* k, const dion3_ns
     for (int i : c) nb += g[i].batch;
     const int kk = k[c[0]], mm = P.m[c[0]];
     P.xbuf = std::max(P.xbuf, al256((size_t)nb * kk * mm * es));
-    P.gram = std::max(P.gram, dion3_gram_ns_workspace_bytes(nb, kk, mm, p->ns_dtype));
+    P.gram = std::max(P.gram, mm == kk ? dion3_standard_ns_workspace_bytes(nb, kk, mm, p->ns_dtype)
+                                       : dion3_gram_ns_workspace_bytes(nb, kk, mm, p->ns_dtype));
   }
   return true;
 }
 
-// The library streams (default priority, not synchronising with the null
-// stream) and an event pool, created on a device's first step and kept until
-// the process ends.  Enqueueing a step holds the mutex, so concurrent callers
-// do not interleave their use of the events.
+// The library streams (default priority) and an event pool, created on a
+// device's first step and kept until the process ends.  Enqueueing a step
+// holds the mutex, so concurrent callers do not interleave their use of the
+// events.  The compute-unit-masked stream is a blocking stream (its creation
+// call takes no flags, so it synchronises with the legacy null stream).
 struct SideCtx {
-  hipStream_t side = nullptr;   // gathers + Newton-Schulz, every compute unit
-  hipStream_t mem = nullptr;    // overlapped HBM-bound passes, half the compute units
+  hipStream_t side = nullptr;   // gathers + Newton-Schulz, every compute unit (non-blocking)
+  hipStream_t mem = nullptr;    // overlapped HBM-bound passes, half the compute units (blocking)
   std::vector<hipEvent_t> ev;
 };
 constexpr int kMaxDevices = 64;
@@ -142,6 +146,12 @@ static int run_step(int n_groups, const dion3_group* groups, void* const* W, voi
   const size_t es = dtype_size(p->ns_dtype);
   hipStream_t s = (hipStream_t)stream;
 
+  // graph capture of the multi-stream step is not supported: refuse before
+  // anything is enqueued
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess) return DION3_ERR_HIP;
+  if (cap != hipStreamCaptureStatusNone) return DION3_ERR_UNSUPPORTED;
+
   std::lock_guard<std::mutex> lock(g_side_mu);
   SideCtx* ctx = nullptr;
   int st = side_ctx(3 * (size_t)nc + 3, &ctx);
@@ -198,7 +208,10 @@ static int run_step(int n_groups, const dion3_group* groups, void* const* W, voi
                              p->ns_dtype, X0 + nb * slice, side);
       nb += gi.batch;
     }
-    if (!st) st = dion3_gram_ns(nb, kk, mm, p, X0, O, gws, P.gram, side);
+    // aspect ratio 1: standard Newton-Schulz on the symmetric kernels (fewer
+    // launches, equal work); otherwise Gram Newton-Schulz
+    if (!st) st = mm == kk ? dion3_standard_ns(nb, kk, mm, p, X0, O, gws, P.gram, side)
+                           : dion3_gram_ns(nb, kk, mm, p, X0, O, gws, P.gram, side);
     if (!st) st = hip_ok(hipEventRecord(ev_ns[c], side));
     hipStream_t uc = upd_stream(c);
     if (!st) st = hip_ok(hipStreamWaitEvent(uc, ev_ns[c], 0));

@@ -65,6 +65,8 @@ def _load() -> ctypes.CDLL:
         "dion3_gather_rows": (i, [gp, vp, vp, i, vp, f, i, vp, vp]),
         "dion3_gram_ns_workspace_bytes": (sz, [i, i, i, i]),
         "dion3_gram_ns": (i, [i, i, i, pp, vp, vp, vp, sz, vp]),
+        "dion3_standard_ns_workspace_bytes": (sz, [i, i, i, i]),
+        "dion3_standard_ns": (i, [i, i, i, pp, vp, vp, vp, sz, vp]),
         "dion3_syrk": (i, [i, i, i, i, vp, ll, vp, ll, f, f, vp]),
         "dion3_sym_sq_add": (i, [i, i, i, vp, ll, vp, ll, vp, ll, f, f, f, vp]),
         "dion3_sym_mul": (i, [i, i, i, vp, ll, vp, ll, vp, ll, f, vp]),
@@ -194,6 +196,19 @@ def dion3_gram_ns(X0, O, params=None, ws=None):
         ws = workspace(dion3_gram_ns_workspace_bytes(b, k, m, p.ns_dtype), X0.device)
     _check(lib.dion3_gram_ns(b, k, m, ctypes.byref(p), _ptr(X0), _ptr(O), _ptr(ws), ws.numel(),
                              _stream()), "dion3_gram_ns")
+
+
+def dion3_standard_ns_workspace_bytes(batch, k, m, ns_dtype) -> int:
+    return lib.dion3_standard_ns_workspace_bytes(batch, k, m, ns_dtype)
+
+
+def dion3_standard_ns(X0, O, params=None, ws=None):
+    b, k, m = X0.shape
+    p = params if params is not None else make_ns_params(ns_dtype=dtype_code(X0.dtype))
+    if ws is None:
+        ws = workspace(dion3_standard_ns_workspace_bytes(b, k, m, p.ns_dtype), X0.device)
+    _check(lib.dion3_standard_ns(b, k, m, ctypes.byref(p), _ptr(X0), _ptr(O), _ptr(ws), ws.numel(),
+                                 _stream()), "dion3_standard_ns")
 
 
 def dion3_syrk(A, C, alpha=1.0, beta=0.0):

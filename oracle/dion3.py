@@ -350,7 +350,9 @@ def dion3_step(W, M, G, *, k: int, mu: float, eta: float, wd: float = 0.0,
     idx = select_rows(keys, k)
     X = M[idx]
     if ns is None:
-        O = ns_gram(X, coeffs, restart_after, eps)
+        # aspect ratio 1 (square selected submatrix): standard Newton-Schulz,
+        # the pages' fall-back (paper §4); Gram Newton-Schulz otherwise
+        O = ns_standard(X, coeffs, eps) if X.shape[0] == X.shape[1] else ns_gram(X, coeffs, restart_after, eps)
     else:
         O = ns(X)
     W, M = apply_rows(W, M, idx, O, eta, wd, mu, fmt)

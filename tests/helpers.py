@@ -32,7 +32,8 @@ def np_bits(x: np.ndarray, dtype: torch.dtype) -> np.ndarray:
 
 def manual_step(d, groups, ks, params, eta, wd, mu, keep=None):
     """The step through the individual entry points, batched like dion3_step
-    (groups of equal canonical (k, m) share one Newton-Schulz call).  Returns
+    (groups of equal canonical (k, m) share one Newton-Schulz call; a square
+    class uses standard Newton-Schulz).  Returns
     per-group idx and the Newton-Schulz output O (canonical orientation) of
     every matrix, or, with keep = {group: [matrix, ...]}, of those only."""
     ns_t = d.torch_dtype(params.ns_dtype)
@@ -55,7 +56,11 @@ def manual_step(d, groups, ks, params, eta, wd, mu, keep=None):
             d.dion3_gather_rows(M, idx, k, sqn, X[off:off + b], eps=params.eps)
             idxs[g] = idx
             off += b
-        d.dion3_gram_ns(X, Ob, params)
+        # like the whole step: standard Newton-Schulz when the class is square
+        if k == m:
+            d.dion3_standard_ns(X, Ob, params)
+        else:
+            d.dion3_gram_ns(X, Ob, params)
         off = 0
         for g in members:
             W, M, G = groups[g]

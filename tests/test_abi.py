@@ -106,6 +106,14 @@ def test_invalid_arguments_rejected_without_launch():
     assert L.dion3_gram_ns(2, 64, 128, pp, FAKE, FAKE, FAKE, wsn, None) == -1          # X0 == O
     bad = d.make_ns_params(T=0, coeffs=[])
     assert L.dion3_gram_ns(2, 64, 128, ctypes.byref(bad), FAKE, ctypes.c_void_p(0x2000), FAKE, wsn, None) == -1
+    # standard_ns: same argument checks
+    wss = L.dion3_standard_ns_workspace_bytes(2, 64, 128, d.F16)
+    assert wss > 0
+    assert L.dion3_standard_ns(2, 129, 128, pp, FAKE, ctypes.c_void_p(0x2000), FAKE, wss, None) == -1
+    assert L.dion3_standard_ns(2, 64, 128, pp, FAKE, ctypes.c_void_p(0x2000), FAKE, wss - 1, None) == -3
+    assert L.dion3_standard_ns(2, 64, 128, pp, FAKE, FAKE, FAKE, wss, None) == -1        # X0 == O
+    assert L.dion3_standard_ns(2, 64, 128, ctypes.byref(bad), FAKE, ctypes.c_void_p(0x2000), FAKE, wss,
+                               None) == -1
     # whole step: workspace query and a too-small workspace
     groups = (d.Group * 2)(d.Group(64, 128, 2, 64 * 128, d.BF16, -1), d.Group(128, 64, 1, 128 * 64, d.BF16, -1))
     ks = (ctypes.c_int * 2)(16, 16)
@@ -127,3 +135,10 @@ def test_gram_ns_workspace_formula():
     for (b, k, m, dt, es) in [(3, 100, 300, d.F16, 2), (1, 256, 1024, d.F32, 4)]:
         al = lambda v: (v + 255) // 256 * 256
         assert L.dion3_gram_ns_workspace_bytes(b, k, m, dt) == al(b * k * m * es) + 4 * al(b * k * k * es)
+
+
+def test_standard_ns_workspace_formula():
+    L = d.lib
+    for (b, k, m, dt, es) in [(3, 100, 300, d.F16, 2), (1, 256, 1024, d.F32, 4)]:
+        al = lambda v: (v + 255) // 256 * 256
+        assert L.dion3_standard_ns_workspace_bytes(b, k, m, dt) == al(b * k * m * es) + 2 * al(b * k * k * es)

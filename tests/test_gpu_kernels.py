@@ -257,6 +257,38 @@ def test_gram_ns_restart_variants(d):
         assert rel_fro(to64(Od)[0], ref) <= 1e-4, mask
 
 
+# ---------------------------------------------------- standard Newton-Schulz
+@pytest.mark.parametrize("xdt,tol", [("f32", 1e-4), ("f16", 3e-2)])
+@pytest.mark.parametrize("b,k,m", [(2, 128, 512), (2, 100, 300), (1, 256, 256), (1, 64, 64)])
+def test_standard_ns(d, xdt, tol, b, k, m):
+    """dion3_standard_ns against the oracle's standard Newton-Schulz."""
+    rng = np.random.default_rng(3 * k + m)
+    X = rng.standard_normal((b, k, m)) * np.exp(rng.standard_normal((b, k, 1)))
+    X0 = np.stack([O.frobenius_normalize(x, 1e-7) for x in X])
+    Xd = torch.from_numpy(X0).to(TD[xdt]).to(DEV)
+    Od = torch.empty_like(Xd)
+    d.dion3_standard_ns(Xd, Od, d.make_ns_params(ns_dtype=d.dtype_code(TD[xdt])))
+    torch.cuda.synchronize()
+    xin = to64(Xd)
+    for i in range(b):
+        err = rel_fro(to64(Od[i]), O.ns_standard(xin[i], eps=0.0))
+        assert err <= tol, err
+
+
+def test_standard_ns_large_tiles(d):
+    """52 square 1024 x 1024 inputs: every product runs on the 256 x 256 kernels
+    (520 symmetric tiles, 832 rectangular tiles); first and last checked."""
+    b, k = 52, 1024
+    Xd = synth.dense(k, k, b, dtype="f16", device=DEV, seed=5)
+    Xd = (Xd.float() / Xd.float().flatten(1).norm(dim=1).view(b, 1, 1)).half()
+    Od = torch.empty_like(Xd)
+    d.dion3_standard_ns(Xd, Od, d.make_ns_params(ns_dtype=d.F16))
+    torch.cuda.synchronize()
+    for i in (0, b - 1):
+        err = rel_fro(to64(Od[i]), O.ns_standard(to64(Xd[i]), eps=0.0))
+        assert err <= 3e-2, (i, err)
+
+
 def test_gemm_deterministic(d):
     A = synth.dense(512, 1024, 2, dtype="f16", device=DEV, seed=1)
     outs = []
