@@ -322,6 +322,36 @@ def apply_rows(W, M, idx, O, eta: float, wd: float, mu: float, fmt: str):
 
 
 # --------------------------------------------------------------------------
+# NorMuon flavour  [paper §2 (NorMuon divides each row of the orthogonalised
+# update by the root of that row's second moment, then rescales the update so
+# that its Frobenius norm is Muon's), §6 (the flavour updates the second
+# moments of the selected rows and rescales O; the normalisation runs in
+# fp32)].  The pages' equation and listing are missing from the extracted
+# text; this is the plainest reading of the prose:
+#   q_i = mean_j O_ij^2;   v_i <- beta2 v_i + (1 - beta2) q_i;
+#   O_hat_i = O_i / (sqrt(v_i) + eps);   O_hat <- O_hat ||O||_F / ||O_hat||_F
+# beta2 and eps are parameters (no values survive in the text); no bias
+# correction.
+# --------------------------------------------------------------------------
+DEFAULT_BETA2 = 0.95
+DEFAULT_NORMUON_EPS = 1e-8
+
+
+def normuon_scale(O, v, beta2: float = DEFAULT_BETA2, eps: float = DEFAULT_NORMUON_EPS):
+    """(O_hat, v_new) for the k selected rows O (k x m) and their second
+    moments v (k); exact arithmetic in fp64."""
+    O = np.asarray(O, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    q = np.sum(O * O, axis=1) / O.shape[1]
+    v_new = beta2 * v + (1.0 - beta2) * q
+    d = 1.0 / (np.sqrt(v_new) + eps)
+    Oh = O * d[:, None]
+    nh = math.sqrt(float(np.sum(Oh * Oh)))
+    r = math.sqrt(float(np.sum(O * O))) / nh if nh > 0.0 else 1.0
+    return Oh * r, v_new
+
+
+# --------------------------------------------------------------------------
 # The whole step on one matrix
 # --------------------------------------------------------------------------
 def canonical_axis(rows: int, cols: int, sel_axis: int = -1) -> int:
@@ -334,11 +364,15 @@ def canonical_axis(rows: int, cols: int, sel_axis: int = -1) -> int:
 def dion3_step(W, M, G, *, k: int, mu: float, eta: float, wd: float = 0.0,
                coeffs=DEFAULT_COEFFS, restart_after=DEFAULT_RESTART_AFTER,
                eps: float = DEFAULT_EPS, fmt: str = "f64", sel_axis: int = -1,
-               ns=None, keys_exact: bool = True):
-    """One Dion3 step (Muon flavour) on a single matrix.
+               ns=None, keys_exact: bool = True, V=None,
+               beta2: float = DEFAULT_BETA2, nm_eps: float = DEFAULT_NORMUON_EPS):
+    """One Dion3 step on a single matrix: the Muon flavour, or the NorMuon
+    flavour when V (the second moment of every line of the selection axis) is
+    given.
 
-    Returns dict(W, M, idx, O, keys) with W, M in stored orientation and
-    idx, O, keys in canonical orientation (selected axis first)."""
+    Returns dict(W, M, idx, O, keys[, V, O_hat]) with W, M in stored
+    orientation and idx, O, keys, V, O_hat in canonical orientation (selected
+    axis first)."""
     W = np.asarray(W, dtype=np.float64)
     M = np.asarray(M, dtype=np.float64)
     G = np.asarray(G, dtype=np.float64)
@@ -355,10 +389,17 @@ def dion3_step(W, M, G, *, k: int, mu: float, eta: float, wd: float = 0.0,
         O = ns_standard(X, coeffs, eps) if X.shape[0] == X.shape[1] else ns_gram(X, coeffs, restart_after, eps)
     else:
         O = ns(X)
-    W, M = apply_rows(W, M, idx, O, eta, wd, mu, fmt)
+    out = {"idx": idx, "O": O, "keys": keys}
+    U = O
+    if V is not None:
+        V = np.array(V, dtype=np.float64)
+        U, V[idx] = normuon_scale(O, V[idx], beta2, nm_eps)
+        out["V"], out["O_hat"] = V, U
+    W, M = apply_rows(W, M, idx, U, eta, wd, mu, fmt)
     if axis == 1:
         W, M = W.T, M.T
-    return {"W": W, "M": M, "idx": idx, "O": O, "keys": keys}
+    out["W"], out["M"] = W, M
+    return out
 
 
 def muon_step(W, M, G, *, mu: float, eta: float, wd: float = 0.0,

@@ -415,3 +415,74 @@ def test_planted_mistakes_are_caught(mistake):
     # and the correct variant passes both
     fine = _gram_variant(X, "none")
     assert rel(fine, good) <= 1e-10 and rel(fine, svd) <= 1e-10
+
+
+# ------------------------------------------------------------ NorMuon flavour
+@pytest.mark.parametrize("shape", [(6, 20), (16, 64)])
+def test_normuon_equal_moments_leave_o_unchanged(shape):
+    """beta2 = 1 keeps v; equal v on every row scales all rows alike, and the
+    Frobenius rescale undoes the common factor: O_hat = O."""
+    Ob = sample(*shape, seed=11)
+    v = np.full(shape[0], 0.37)
+    Oh, vn = O.normuon_scale(Ob, v, beta2=1.0, eps=1e-3)
+    assert np.array_equal(vn, v)
+    assert rel(Oh, Ob) <= 1e-14
+
+
+@pytest.mark.parametrize("beta2", [0.0, 0.5, 0.95])
+def test_normuon_balances_row_norms(beta2):
+    """v = 0 and eps = 0: the new moment is (1 - beta2) times each row's mean
+    square, so every row of O_hat has the same norm, and ||O_hat||_F = ||O||_F."""
+    Ob = sample(8, 32, seed=12)          # rows of very different norms
+    Oh, vn = O.normuon_scale(Ob, np.zeros(8), beta2=beta2, eps=0.0)
+    rows = np.linalg.norm(Oh, axis=1)
+    assert np.ptp(rows) <= 1e-12 * rows.max()
+    assert abs(np.linalg.norm(Oh) - np.linalg.norm(Ob)) <= 1e-12 * np.linalg.norm(Ob)
+    assert rel(vn, (1.0 - beta2) * np.mean(Ob * Ob, axis=1)) <= 1e-15
+
+
+def test_normuon_moment_is_an_ema():
+    """beta2 = 0 makes v this step's row mean square; beta2 = 1 keeps it."""
+    Ob = sample(5, 9, seed=13)
+    v = np.arange(1.0, 6.0)
+    assert rel(O.normuon_scale(Ob, v, beta2=0.0)[1], np.mean(Ob ** 2, axis=1)) <= 1e-15
+    assert np.array_equal(O.normuon_scale(Ob, v, beta2=1.0)[1], v)
+
+
+@pytest.mark.parametrize("mistake", ["no_rescale", "no_row_scale", "sum_not_mean"])
+def test_normuon_planted_mistakes_are_caught(mistake):
+    def variant(Ob, v, beta2, eps):
+        q = np.sum(Ob * Ob, axis=1) / (1.0 if mistake == "sum_not_mean" else Ob.shape[1])
+        vn = beta2 * v + (1.0 - beta2) * q
+        d = np.ones_like(vn) if mistake == "no_row_scale" else 1.0 / (np.sqrt(vn) + eps)
+        Oh = Ob * d[:, None]
+        if mistake != "no_rescale":
+            Oh *= np.linalg.norm(Ob) / np.linalg.norm(Oh)
+        return Oh, vn
+    Ob = 3.0 * sample(8, 32, seed=14)
+    ok = []
+    # the three pins above, applied to the variant
+    Oh, vn = variant(Ob, np.full(8, 0.37), 1.0, 1e-3)
+    ok.append(rel(Oh, Ob) <= 1e-14)
+    Oh, vn = variant(Ob, np.zeros(8), 0.5, 0.0)
+    rows = np.linalg.norm(Oh, axis=1)
+    ok.append(np.ptp(rows) <= 1e-12 * rows.max()
+              and abs(np.linalg.norm(Oh) - np.linalg.norm(Ob)) <= 1e-12 * np.linalg.norm(Ob))
+    ok.append(rel(variant(Ob, np.arange(1.0, 9.0), 0.0, 1e-8)[1], np.mean(Ob ** 2, axis=1)) <= 1e-15)
+    assert not all(ok)
+
+
+def test_normuon_step_untouched_lines_and_moments():
+    """The NorMuon step changes V only on the selected lines, and W and M only
+    on the selected lines (canonical orientation)."""
+    rng = np.random.default_rng(15)
+    W, M, G = rng.standard_normal((3, 24, 10))        # rows > cols: columns selected
+    V = np.abs(rng.standard_normal(10))
+    out = O.dion3_step(W, M, G, k=4, mu=0.9, eta=0.1, V=V)
+    sel = np.zeros(10, dtype=bool)
+    sel[out["idx"]] = True
+    assert np.array_equal(out["V"][~sel], V[~sel])
+    assert np.all(out["V"][sel] != V[sel])
+    assert np.array_equal(out["W"][:, ~sel], W[:, ~sel])
+    assert np.array_equal(out["M"][:, ~sel], (M + G)[:, ~sel])
+    assert abs(np.linalg.norm(out["O_hat"]) - np.linalg.norm(out["O"])) <= 1e-12 * np.linalg.norm(out["O"])
