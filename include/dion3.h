@@ -199,6 +199,29 @@ int dion3_apply_rows(const dion3_group* g, void* W, void* M, const int32_t* idx,
                      const void* O, int o_dtype, long long o_stride,
                      float eta, float wd, float mu, void* stream);
 
+/* dion3_apply_rows with a factor per row of O (the NorMuon flavour): every
+ * selected line uses fp32(row_scale[b][i] * O[b][i][j]) in place of O[b][i][j]
+ * (one fp32 product, then the same fused update).  row_scale [batch][k] fp32,
+ * may be NULL (then exactly dion3_apply_rows). */
+int dion3_apply_rows_scaled(const dion3_group* g, void* W, void* M, const int32_t* idx, int k,
+                            const void* O, int o_dtype, long long o_stride, const float* row_scale,
+                            float eta, float wd, float mu, void* stream);
+
+/* NorMuon flavour (Section 2: each row of the orthogonalised update is divided
+ * by the root of its second moment, an exponential moving average, and the
+ * update is rescaled to Muon's Frobenius norm; Section 6: only the selected
+ * lines' moments are updated, in fp32).  Per matrix b, selected row i:
+ *   q = sum_j O_ij^2 / m;  V[b][idx_i] <- fma(beta2, V[b][idx_i], fp32(1-beta2) * q)
+ *   d_i = 1 / (sqrt(V[b][idx_i]) + eps);  r = ||O||_F / ||diag(d) O||_F (1 if 0)
+ *   row_scale[b][i] = d_i r
+ *   O    [batch] slices of [k][m] (o_stride elements apart), canonical, F16 or F32.
+ *   V    in/out [batch][n] fp32: second moment of every line of the selection axis.
+ *   row_scale out [batch][k] fp32, for dion3_apply_rows_scaled.
+ * 0 <= beta2 <= 1, eps >= 0.  Deterministic (fixed-order reductions). */
+int dion3_normuon_scale(const dion3_group* g, const int32_t* idx, int k, const void* O, int o_dtype,
+                        long long o_stride, float* V, float beta2, float eps, float* row_scale,
+                        void* stream);
+
 /* The error-feedback decay alone, M[S,:] <- round(mu * M[S,:]) for the lines
  * in idx ([batch][k] ascending), one rounding (Section 6).  Completes a
  * deferred decay, e.g. before M is read or saved. */
@@ -234,7 +257,8 @@ size_t dion3_step_workspace_bytes(int n_groups, const dion3_group* groups, const
  * as if all of it had been enqueued there; `stream` must belong to the
  * current device.  Concurrent calls on one device are serialised while they
  * enqueue.  The workspace (dion3_step_workspace_bytes) holds the selected
- * sums of squares of every group and, with two or more (k, m) classes, two
+ * sums of squares and the NorMuon row factors of every group and, with two or
+ * more (k, m) classes, two
  * Newton-Schulz outputs so that one class's update overlaps the next class. */
 int dion3_step(int n_groups, const dion3_group* groups, void* const* W, void* const* M,
                const void* const* G, const int* k, int32_t* const* idx,
@@ -252,6 +276,17 @@ int dion3_step_deferred(int n_groups, const dion3_group* groups, void* const* W,
                         const void* const* G, const int* k, int32_t* const* idx, int has_prev,
                         const dion3_ns_params* p, float eta, float wd, float mu,
                         void* ws, size_t ws_bytes, void* stream);
+
+/* The whole step in the NorMuon flavour: dion3_step (deferred = 0) or
+ * dion3_step_deferred (deferred = 1, has_prev as there) with
+ * dion3_normuon_scale before each group's update.  V[i] is group i's
+ * [batch][n] fp32 second-moment state (zero before the first step); beta2 and
+ * nm_eps as in dion3_normuon_scale.  Same streams, workspace query and
+ * capture restriction as dion3_step. */
+int dion3_step_normuon(int n_groups, const dion3_group* groups, void* const* W, void* const* M,
+                       const void* const* G, const int* k, int32_t* const* idx, float* const* V,
+                       int deferred, int has_prev, const dion3_ns_params* p, float eta, float wd,
+                       float mu, float beta2, float nm_eps, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------ measurement */
 

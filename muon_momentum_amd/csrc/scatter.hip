@@ -119,9 +119,10 @@ __global__ __launch_bounds__(256) void gather_cols_kernel(
 template <typename TS, typename TO, bool VEC>
 __global__ __launch_bounds__(256) void apply_rows_kernel(
     TS* __restrict__ W, TS* __restrict__ M, long long bstride, int nlines, int cols,
-    const int32_t* __restrict__ idx, int k, const TO* __restrict__ O, long long ostride, float eta,
-    float u_, int decay, float mu) {
-  // W == nullptr: decay M only; M == nullptr: update W only (decay deferred)
+    const int32_t* __restrict__ idx, int k, const TO* __restrict__ O, long long ostride,
+    const float* __restrict__ rs, float eta, float u_, int decay, float mu) {
+  // W == nullptr: decay M only; M == nullptr: update W only (decay deferred);
+  // rs (may be NULL): a factor per row of O (NorMuon), one fp32 product
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = blockIdx.x * 4 + wave;
@@ -132,6 +133,7 @@ __global__ __launch_bounds__(256) void apply_rows_kernel(
   TS* w = dw ? W + b * bstride + (long long)r * cols : nullptr;
   TS* mm = dm ? M + b * bstride + (long long)r * cols : nullptr;
   const TO* o = dw ? O + b * ostride + (long long)i * cols : nullptr;
+  const float f = (dw && rs) ? rs[(long long)b * k + i] : 1.f;   // x * 1 is exact
   if (VEC) {
     // U chunks of 512 elements per wave in flight: all loads first, then stores
     constexpr int U = 4;
@@ -153,7 +155,7 @@ __global__ __launch_bounds__(256) void apply_rows_kernel(
           if (dw) {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-              vw[u].e[e] = update_w<TS>(vw[u].e[e], Store<TO>::to_f32(vo[u].e[e]), eta, u_, decay != 0);
+              vw[u].e[e] = update_w<TS>(vw[u].e[e], Store<TO>::to_f32(vo[u].e[e]) * f, eta, u_, decay != 0);
             store8<TS>(w + c, vw[u]);
           }
           if (dm) {
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(256) void apply_rows_kernel(
     }
   } else {
     for (int c = lane; c < cols; c += 64) {
-      if (dw) w[c] = update_w<TS>(w[c], Store<TO>::to_f32(o[c]), eta, u_, decay != 0);
+      if (dw) w[c] = update_w<TS>(w[c], Store<TO>::to_f32(o[c]) * f, eta, u_, decay != 0);
       if (dm) mm[c] = decay_round<TS>(mu, mm[c]);
     }
   }
@@ -178,7 +180,7 @@ template <typename TS, typename TO>
 __global__ __launch_bounds__(256) void apply_cols_kernel(
     TS* __restrict__ W, TS* __restrict__ M, long long bstride, int rows, int cols,
     const int32_t* __restrict__ idx, int k, const TO* __restrict__ O, long long ostride,
-    float eta, float u, int decay, float mu) {
+    const float* __restrict__ rs, float eta, float u, int decay, float mu) {
   __shared__ float tile[64][65];
   const int b = blockIdx.z;
   const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
@@ -191,7 +193,8 @@ __global__ __launch_bounds__(256) void apply_cols_kernel(
       const int il2 = (t >> 6) + 4 * s;
       const int jl = t & 63;
       const int i = i0 + il2, j = j0 + jl;
-      tile[il2][jl] = (i < k && j < rows) ? Store<TO>::to_f32(Ob[(long long)i * rows + j]) : 0.f;
+      const float f = (rs && i < k) ? rs[(long long)b * k + i] : 1.f;   // x * 1 is exact
+      tile[il2][jl] = (i < k && j < rows) ? Store<TO>::to_f32(Ob[(long long)i * rows + j]) * f : 0.f;
     }
   }
   __syncthreads();
@@ -264,8 +267,8 @@ static void launch_gather(const dion3_group* g, int axis, int n, int m, const vo
 
 template <typename TS, typename TO>
 static void launch_apply(const dion3_group* g, int axis, int n, int m, void* W, void* M,
-                         const int32_t* idx, int k, const void* O, long long ostride, float eta,
-                         float wd, float mu, hipStream_t s) {
+                         const int32_t* idx, int k, const void* O, long long ostride, const float* rs,
+                         float eta, float wd, float mu, hipStream_t s) {
   // u = fp32(1 - eta wd): the product is exact in fp64, one rounding to fp32
   const float u = (float)(1.0 - (double)eta * (double)wd);
   const int decay = wd != 0.0f;
@@ -281,15 +284,15 @@ static void launch_apply(const dion3_group* g, int axis, int n, int m, void* W, 
     dim3 grid((k + 3) / 4, g->batch);
     if (vec)
       hipLaunchKernelGGL((apply_rows_kernel<TS, TO, true>), grid, dim3(256), 0, s, (TS*)W, (TS*)M,
-                         g->batch_stride, n, m, idx, k, (const TO*)O, ostride, eta, u, decay, mu);
+                         g->batch_stride, n, m, idx, k, (const TO*)O, ostride, rs, eta, u, decay, mu);
     else
       hipLaunchKernelGGL((apply_rows_kernel<TS, TO, false>), grid, dim3(256), 0, s, (TS*)W, (TS*)M,
-                         g->batch_stride, n, m, idx, k, (const TO*)O, ostride, eta, u, decay, mu);
+                         g->batch_stride, n, m, idx, k, (const TO*)O, ostride, rs, eta, u, decay, mu);
   } else {
     dim3 grid((m + 63) / 64, (k + 63) / 64, g->batch);
     hipLaunchKernelGGL((apply_cols_kernel<TS, TO>), grid, dim3(256), 0, s, (TS*)W, (TS*)M,
-                       g->batch_stride, g->rows, g->cols, idx, k, (const TO*)O, ostride, eta, u, decay,
-                       mu);
+                       g->batch_stride, g->rows, g->cols, idx, k, (const TO*)O, ostride, rs, eta, u,
+                       decay, mu);
   }
 }
 
@@ -317,26 +320,34 @@ extern "C" int dion3_gather_rows(const dion3_group* g, const void* M, const int3
   return launch_status();
 }
 
-extern "C" int dion3_apply_rows(const dion3_group* g, void* W, void* M, const int32_t* idx, int k,
-                                const void* O, int o_dtype, long long o_stride, float eta, float wd,
-                                float mu, void* stream) {
+extern "C" int dion3_apply_rows_scaled(const dion3_group* g, void* W, void* M, const int32_t* idx,
+                                       int k, const void* O, int o_dtype, long long o_stride,
+                                       const float* row_scale, float eta, float wd, float mu,
+                                       void* stream) {
   int n, m, axis;
   if (!canonical_dims(g, &n, &m, &axis)) return DION3_ERR_INVALID_ARG;
-  if (!W || !idx || !O || k < 1 || k > n) return DION3_ERR_INVALID_ARG;   // M may be NULL
+  if (!W || !idx || !O || k < 1 || k > n) return DION3_ERR_INVALID_ARG;   // M, row_scale may be NULL
   if (g->batch > 1 && o_stride < (long long)k * m) return DION3_ERR_INVALID_ARG;
   if (n > 32768) return DION3_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
+  const float* rs = row_scale;
   if (g->dtype == DION3_BF16 && o_dtype == DION3_F16)
-    launch_apply<bf16_t, f16>(g, axis, n, m, W, M, idx, k, O, o_stride, eta, wd, mu, s);
+    launch_apply<bf16_t, f16>(g, axis, n, m, W, M, idx, k, O, o_stride, rs, eta, wd, mu, s);
   else if (g->dtype == DION3_BF16 && o_dtype == DION3_F32)
-    launch_apply<bf16_t, float>(g, axis, n, m, W, M, idx, k, O, o_stride, eta, wd, mu, s);
+    launch_apply<bf16_t, float>(g, axis, n, m, W, M, idx, k, O, o_stride, rs, eta, wd, mu, s);
   else if (g->dtype == DION3_F32 && o_dtype == DION3_F32)
-    launch_apply<float, float>(g, axis, n, m, W, M, idx, k, O, o_stride, eta, wd, mu, s);
+    launch_apply<float, float>(g, axis, n, m, W, M, idx, k, O, o_stride, rs, eta, wd, mu, s);
   else if (g->dtype == DION3_F32 && o_dtype == DION3_F16)
-    launch_apply<float, f16>(g, axis, n, m, W, M, idx, k, O, o_stride, eta, wd, mu, s);
+    launch_apply<float, f16>(g, axis, n, m, W, M, idx, k, O, o_stride, rs, eta, wd, mu, s);
   else
     return DION3_ERR_INVALID_ARG;
   return launch_status();
+}
+
+extern "C" int dion3_apply_rows(const dion3_group* g, void* W, void* M, const int32_t* idx, int k,
+                                const void* O, int o_dtype, long long o_stride, float eta, float wd,
+                                float mu, void* stream) {
+  return dion3_apply_rows_scaled(g, W, M, idx, k, O, o_dtype, o_stride, nullptr, eta, wd, mu, stream);
 }
 
 extern "C" int dion3_decay_rows(const dion3_group* g, void* M, const int32_t* idx, int k, float mu,
@@ -347,9 +358,9 @@ extern "C" int dion3_decay_rows(const dion3_group* g, void* M, const int32_t* id
   if (n > 32768) return DION3_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
   if (g->dtype == DION3_BF16)
-    launch_apply<bf16_t, bf16_t>(g, axis, n, m, nullptr, M, idx, k, nullptr, 0, 0.f, 0.f, mu, s);
+    launch_apply<bf16_t, bf16_t>(g, axis, n, m, nullptr, M, idx, k, nullptr, 0, nullptr, 0.f, 0.f, mu, s);
   else if (g->dtype == DION3_F32)
-    launch_apply<float, float>(g, axis, n, m, nullptr, M, idx, k, nullptr, 0, 0.f, 0.f, mu, s);
+    launch_apply<float, float>(g, axis, n, m, nullptr, M, idx, k, nullptr, 0, nullptr, 0.f, 0.f, mu, s);
   else
     return DION3_ERR_INVALID_ARG;
   return launch_status();

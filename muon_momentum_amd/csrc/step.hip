@@ -3,7 +3,7 @@
 //
 // Method: "Dion3: Full-Stack Orthogonal Updates", Section 6 (update rule),
 // Section 7 (megabatching: every matrix of one shape is processed as one
-// batch) and Section 4 (a class whose selected submatrices are square uses
+// batch), Section 2 for the NorMuon flavour, and Section 4 (a class whose selected submatrices are square uses
 // standard Newton-Schulz on the symmetric kernels, Gram Newton-Schulz
 // otherwise).  On one GPU the batching is across launches: matrices whose selected
 // submatrices have the same (k, m) share one Newton-Schulz batch, so an
@@ -34,13 +34,14 @@ struct Plan {
   std::vector<int> n, m, axis;
   std::vector<std::vector<int>> classes;   // groups sharing (k, m), in order of first appearance
   std::vector<size_t> sqn_off;             // per group: offset of its [batch] fp64 slot
-  size_t rowsel = 0, sqn = 0, xbuf = 0, gram = 0;
-  size_t bytes() const { return rowsel + sqn + (classes.size() > 1 ? 3 : 2) * xbuf + gram; }
+  std::vector<size_t> rs_off;              // per group: offset of its [batch][k] fp32 row factors
+  size_t rowsel = 0, sqn = 0, rs = 0, xbuf = 0, gram = 0;
+  size_t bytes() const { return rowsel + sqn + rs + (classes.size() > 1 ? 3 : 2) * xbuf + gram; }
 };
 
 static bool make_plan(int ng, const dion3_group* g, const int* k, const dion3_ns_params* p, Plan& P) {
   if (ng < 1 || !g || !k || !p) return false;
-  P.n.resize(ng); P.m.resize(ng); P.axis.resize(ng); P.sqn_off.resize(ng);
+  P.n.resize(ng); P.m.resize(ng); P.axis.resize(ng); P.sqn_off.resize(ng); P.rs_off.resize(ng);
   const size_t es = dtype_size(p->ns_dtype);
   if (!es) return false;
   for (int i = 0; i < ng; ++i) {
@@ -49,6 +50,8 @@ static bool make_plan(int ng, const dion3_group* g, const int* k, const dion3_ns
     P.rowsel = std::max(P.rowsel, al256(dion3_rowsel_workspace_bytes(&g[i])));
     P.sqn_off[i] = P.sqn;
     P.sqn += al256(g[i].batch * sizeof(double));
+    P.rs_off[i] = P.rs;
+    P.rs += al256((size_t)g[i].batch * k[i] * sizeof(float));
     bool placed = false;
     for (auto& c : P.classes)
       if (k[c[0]] == k[i] && P.m[c[0]] == P.m[i]) { c.push_back(i); placed = true; break; }
@@ -124,14 +127,18 @@ extern "C" size_t dion3_step_workspace_bytes(int n_groups, const dion3_group* gr
   return P.bytes();
 }
 
+// V == nullptr: Muon flavour; otherwise NorMuon with the per-line second
+// moments V[i] ([batch][n] fp32 per group), beta2 and nm_eps.
 static int run_step(int n_groups, const dion3_group* groups, void* const* W, void* const* M,
                     const void* const* G, const int* k, int32_t* const* idx,
                     const dion3_ns_params* p, float eta, float wd, float mu, void* ws,
-                    size_t ws_bytes, void* stream, bool deferred, bool has_prev) {
+                    size_t ws_bytes, void* stream, bool deferred, bool has_prev,
+                    float* const* V = nullptr, float beta2 = 0.f, float nm_eps = 0.f) {
   Plan P;
   if (!W || !M || !G || !idx || !make_plan(n_groups, groups, k, p, P)) return DION3_ERR_INVALID_ARG;
   for (int i = 0; i < n_groups; ++i)
-    if (!W[i] || !M[i] || !G[i] || !idx[i]) return DION3_ERR_INVALID_ARG;
+    if (!W[i] || !M[i] || !G[i] || !idx[i] || (V && !V[i])) return DION3_ERR_INVALID_ARG;
+  if (V && (!(beta2 >= 0.f && beta2 <= 1.f) || !(nm_eps >= 0.f))) return DION3_ERR_INVALID_ARG;
   if (!ws || ws_bytes < P.bytes()) return DION3_ERR_WORKSPACE;
   const int nc = (int)P.classes.size();
   // workspace: top-k partials | per-group selected sums of squares | X0 |
@@ -140,7 +147,8 @@ static int run_step(int n_groups, const dion3_group* groups, void* const* W, voi
   char* base = (char*)ws;
   char* rs_ws = base;
   char* sqn_base = rs_ws + P.rowsel;
-  char* X0 = sqn_base + P.sqn;
+  char* rsc_base = sqn_base + P.sqn;
+  char* X0 = rsc_base + P.rs;
   char* Obuf[2] = {X0 + P.xbuf, X0 + (nc > 1 ? 2 : 1) * P.xbuf};
   char* gws = X0 + (nc > 1 ? 3 : 2) * P.xbuf;
   const size_t es = dtype_size(p->ns_dtype);
@@ -219,8 +227,13 @@ static int run_step(int n_groups, const dion3_group* groups, void* const* W, voi
     for (int i : cls) {
       if (st) break;
       const dion3_group& gi = groups[i];
-      st = dion3_apply_rows(&gi, W[i], deferred ? nullptr : M[i], idx[i], kk, O + nb * slice, p->ns_dtype,
-                            (long long)kk * mm, eta, wd, mu, uc);
+      float* rsc = V ? (float*)(rsc_base + P.rs_off[i]) : nullptr;
+      if (V)
+        st = dion3_normuon_scale(&gi, idx[i], kk, O + nb * slice, p->ns_dtype, (long long)kk * mm, V[i],
+                                 beta2, nm_eps, rsc, uc);
+      if (!st)
+        st = dion3_apply_rows_scaled(&gi, W[i], deferred ? nullptr : M[i], idx[i], kk, O + nb * slice,
+                                     p->ns_dtype, (long long)kk * mm, rsc, eta, wd, mu, uc);
       nb += gi.batch;
     }
     if (!st) st = hip_ok(hipEventRecord(ev_upd[c], uc));
@@ -251,4 +264,14 @@ extern "C" int dion3_step_deferred(int n_groups, const dion3_group* groups, void
                                    void* stream) {
   return run_step(n_groups, groups, W, M, G, k, idx, p, eta, wd, mu, ws, ws_bytes, stream, true,
                   has_prev != 0);
+}
+
+extern "C" int dion3_step_normuon(int n_groups, const dion3_group* groups, void* const* W,
+                                  void* const* M, const void* const* G, const int* k,
+                                  int32_t* const* idx, float* const* V, int deferred, int has_prev,
+                                  const dion3_ns_params* p, float eta, float wd, float mu,
+                                  float beta2, float nm_eps, void* ws, size_t ws_bytes, void* stream) {
+  if (!V) return DION3_ERR_INVALID_ARG;
+  return run_step(n_groups, groups, W, M, G, k, idx, p, eta, wd, mu, ws, ws_bytes, stream,
+                  deferred != 0, deferred != 0 && has_prev != 0, V, beta2, nm_eps);
 }

@@ -72,6 +72,11 @@ def _load() -> ctypes.CDLL:
         "dion3_sym_mul": (i, [i, i, i, vp, ll, vp, ll, vp, ll, f, vp]),
         "dion3_gemm": (i, [i, i, i, i, vp, ll, vp, ll, i, vp, ll, f, vp]),
         "dion3_apply_rows": (i, [gp, vp, vp, vp, i, vp, i, ll, f, f, f, vp]),
+        "dion3_apply_rows_scaled": (i, [gp, vp, vp, vp, i, vp, i, ll, vp, f, f, f, vp]),
+        "dion3_normuon_scale": (i, [gp, vp, i, vp, i, ll, vp, f, f, vp, vp]),
+        "dion3_step_normuon": (i, [i, gp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                   ctypes.POINTER(i), ctypes.POINTER(vp), ctypes.POINTER(vp), i, i, pp,
+                                   f, f, f, f, f, vp, sz, vp]),
         "dion3_step_workspace_bytes": (sz, [i, gp, ctypes.POINTER(i), pp]),
         "dion3_step": (i, [i, gp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
                            ctypes.POINTER(i), ctypes.POINTER(vp), pp, f, f, f, vp, sz, vp]),
@@ -242,6 +247,23 @@ def dion3_apply_rows(W, M, idx, k, O, eta, wd, mu, sel_axis=-1):
            "dion3_apply_rows")
 
 
+def dion3_normuon_scale(M, idx, k, O, V, row_scale, beta2=0.95, eps=1e-8, sel_axis=-1):
+    """NorMuon row factors of the canonical Newton-Schulz output O [batch][k][m]
+    of the group whose tensor is M; V [batch][n] fp32 is updated in place."""
+    g = make_group(M, sel_axis)
+    _check(lib.dion3_normuon_scale(ctypes.byref(g), _ptr(idx), k, _ptr(O), dtype_code(O.dtype),
+                                   O.stride(0), _ptr(V), beta2, eps, _ptr(row_scale), _stream()),
+           "dion3_normuon_scale")
+
+
+def dion3_apply_rows_scaled(W, M, idx, k, O, row_scale, eta, wd, mu, sel_axis=-1):
+    g = make_group(W, sel_axis)
+    _check(lib.dion3_apply_rows_scaled(ctypes.byref(g), _ptr(W), _ptr(M) if M is not None else None,
+                                       _ptr(idx), k, _ptr(O), dtype_code(O.dtype), O.stride(0),
+                                       _ptr(row_scale) if row_scale is not None else None,
+                                       eta, wd, mu, _stream()), "dion3_apply_rows_scaled")
+
+
 class StepPlan:
     """Marshalled arguments of dion3_step for a fixed list of group tensors."""
 
@@ -274,6 +296,15 @@ class StepPlan:
         _check(lib.dion3_step_deferred(self.n, self.groups, self.W, self.M, self.G, self.k, self.idx,
                                        1 if has_prev else 0, ctypes.byref(self.params), eta, wd, mu,
                                        _ptr(self.ws), self.ws.numel(), _stream()), "dion3_step_deferred")
+
+    def step_normuon(self, Vs, eta, wd, mu, beta2=0.95, nm_eps=1e-8, deferred=False, has_prev=False):
+        """dion3_step_normuon with the per-group second moments Vs ([batch][n]
+        fp32 each, updated in place)."""
+        V = (ctypes.c_void_p * self.n)(*[v.data_ptr() for v in Vs])
+        _check(lib.dion3_step_normuon(self.n, self.groups, self.W, self.M, self.G, self.k, self.idx, V,
+                                      1 if deferred else 0, 1 if has_prev else 0, ctypes.byref(self.params),
+                                      eta, wd, mu, beta2, nm_eps, _ptr(self.ws), self.ws.numel(),
+                                      _stream()), "dion3_step_normuon")
 
     def flush_decay(self, mu):
         """Complete the pending decay of the last deferred step on every group."""
