@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--set", default="7b", choices=["1b", "7b", "14b"])
     ap.add_argument("--f", type=float, default=0.25)
+    ap.add_argument("--flavor", default="muon", choices=["muon", "normuon"],
+                    help="update flavour (NorMuon: beta2 = 0.95, eps = 1e-8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-microbench", action="store_true")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
@@ -92,7 +94,7 @@ def kernel_work(groups, ks, ns_bytes=2, store_bytes=2):
     triangle (k(k+1)/2 entries, 2 x contraction length each); Q X is a full
     k x k by k x m product.  Returns {name: (kind, units per step)}."""
     w = {"momentum_keys": 0.0, "topk_select": 0.0, "gather_scale": 0.0, "apply_update": 0.0,
-         "syrk": 0.0, "sym_sq_add": 0.0, "sym_mul": 0.0, "gemm_qx": 0.0}
+         "syrk": 0.0, "sym_sq_add": 0.0, "sym_mul": 0.0, "gemm_qx": 0.0, "normuon_scale": 0.0}
     for (rows, cols, b), k in zip(groups, ks):
         n, m = min(rows, cols), max(rows, cols)
         w["momentum_keys"] += b * rows * cols * 3 * store_bytes
@@ -100,16 +102,24 @@ def kernel_work(groups, ks, ns_bytes=2, store_bytes=2):
         w["gather_scale"] += b * k * m * (store_bytes + ns_bytes)
         w["apply_update"] += b * k * m * (2 * store_bytes + ns_bytes)
         tri = k * (k + 1) / 2
-        passes, iters = 2, 5                     # restart after iteration 2
-        w["syrk"] += b * passes * tri * 2 * m
-        w["sym_sq_add"] += b * iters * tri * 2 * k
-        # Q products: one per iteration except a pass's first (3); Z R Z: two
-        # products per iteration except a pass's last (3 iterations -> 6)
-        w["sym_mul"] += b * (3 + 6) * tri * 2 * k
-        w["gemm_qx"] += b * passes * 2 * k * k * m
+        if k == m:
+            # square class: standard Newton-Schulz, per iteration X X^T, A^2 + B, Z X
+            w["syrk"] += b * 5 * tri * 2 * m
+            w["sym_sq_add"] += b * 5 * tri * 2 * k
+            w["gemm_qx"] += b * 5 * 2 * k * k * m
+        else:
+            passes, iters = 2, 5                     # restart after iteration 2
+            w["syrk"] += b * passes * tri * 2 * m
+            w["sym_sq_add"] += b * iters * tri * 2 * k
+            # Q products: one per iteration except a pass's first (3); Z R Z: two
+            # products per iteration except a pass's last (3 iterations -> 6)
+            w["sym_mul"] += b * (3 + 6) * tri * 2 * k
+            w["gemm_qx"] += b * passes * 2 * k * k * m
+        # NorMuon flavour: read O once, then the moments and factors
+        w["normuon_scale"] += b * k * (m * ns_bytes + 4 * 4)
     kind = {"momentum_keys": "hbm", "topk_select": "hbm", "gather_scale": "hbm",
             "apply_update": "hbm", "syrk": "mfma", "sym_sq_add": "mfma", "sym_mul": "mfma",
-            "gemm_qx": "mfma"}
+            "gemm_qx": "mfma", "normuon_scale": "hbm"}
     return {name: (kind[name], v) for name, v in w.items()}
 
 
@@ -167,8 +177,16 @@ def run_step_bench(d, synth, torch, args):
 
     # deferred error feedback: each step's momentum pass applies the decay the
     # previous step's selection owes (bit-identical to decaying in the update)
+    Vs = [torch.zeros(b, min(r, c), dtype=torch.float32, device=dev) for r, c, b in groups]
+
+    def one_step(has_prev):
+        if args.flavor == "normuon":
+            plan.step_normuon(Vs, eta, 0.0, MU, deferred=True, has_prev=has_prev)
+        else:
+            plan.step_deferred(eta, 0.0, MU, has_prev=has_prev)
+
     for w in range(args.warmup):
-        plan.step_deferred(eta, 0.0, MU, has_prev=w > 0)
+        one_step(w > 0)
     torch.cuda.synchronize()
     print("# warmup done", file=sys.stderr, flush=True)
 
@@ -180,7 +198,7 @@ def run_step_bench(d, synth, torch, args):
     torch.cuda.synchronize()
     ev[0].record()
     for i in range(args.steps):
-        plan.step_deferred(eta, 0.0, MU, has_prev=args.warmup > 0 or i > 0)
+        one_step(args.warmup > 0 or i > 0)
         ev[i + 1].record()
     torch.cuda.synchronize()
     ms = ev[0].elapsed_time(ev[-1]) / args.steps
@@ -208,7 +226,7 @@ def run_step_bench(d, synth, torch, args):
                        "avg_launch_us": round(avg_us, 2), "bound": kind,
                        "algorithmic_per_launch": units / launches if launches else 0.0,
                        "achieved": round(ach, 2), "unit": unit, "frac": round(ach / peak, 4)}
-    del plan, Ws, Ms, Gs, idxs
+    del plan, Ws, Ms, Gs, idxs, Vs
     torch.cuda.empty_cache()
     return ms, pct, table, groups, ks, eta
 
@@ -295,7 +313,9 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "ms_per_step_p50": round(pct["p50"], 3), "ms_per_step_p90": round(pct["p90"], 3),
         "data": "synthetic (Gaussian gradients with log-normal line scales, seeded)",
-        "config": {"workload": f"{args.set} shape set Dion3 step, f={args.f:g}",
+        "config": {"workload": f"{args.set} shape set Dion3 step, f={args.f:g}"
+                               + ("" if args.flavor == "muon" else ", NorMuon flavour"),
+                   "flavor": args.flavor,
                    "storage": "bf16 W, M, G; f16 Newton-Schulz (fp32 accumulation)",
                    "groups": [list(g) for g in groups], "k": ks, "T": 5, "restart_after": 2,
                    "mu": MU, "eta": eta},
