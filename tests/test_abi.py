@@ -142,3 +142,47 @@ def test_standard_ns_workspace_formula():
     for (b, k, m, dt, es) in [(3, 100, 300, d.F16, 2), (1, 256, 1024, d.F32, 4)]:
         al = lambda v: (v + 255) // 256 * 256
         assert L.dion3_standard_ns_workspace_bytes(b, k, m, dt) == al(b * k * m * es) + 2 * al(b * k * k * es)
+
+
+def test_normuon_entry_points_reject_invalid_arguments():
+    """NorMuon scale, scaled update and NorMuon step: argument checks that fail
+    before anything is launched (no GPU needed)."""
+    L = d.lib
+    g = d.Group(64, 300, 2, 64 * 300, d.BF16, -1)          # n = 64, m = 300
+    gp = ctypes.byref(g)
+    P2 = ctypes.c_void_p(0x2000)
+    # normuon_scale: null pointers, k outside [1, n], beta2 outside [0, 1], eps < 0, dtype, stride
+    assert L.dion3_normuon_scale(gp, None, 8, FAKE, d.F16, 8 * 300, P2, 0.95, 1e-8, P2, None) == -1
+    assert L.dion3_normuon_scale(gp, FAKE, 8, FAKE, d.F16, 8 * 300, None, 0.95, 1e-8, P2, None) == -1
+    assert L.dion3_normuon_scale(gp, FAKE, 8, FAKE, d.F16, 8 * 300, P2, 0.95, 1e-8, None, None) == -1
+    assert L.dion3_normuon_scale(gp, FAKE, 0, FAKE, d.F16, 8 * 300, P2, 0.95, 1e-8, P2, None) == -1
+    assert L.dion3_normuon_scale(gp, FAKE, 65, FAKE, d.F16, 65 * 300, P2, 0.95, 1e-8, P2, None) == -1
+    assert L.dion3_normuon_scale(gp, FAKE, 8, FAKE, d.F16, 8 * 300, P2, 1.5, 1e-8, P2, None) == -1
+    assert L.dion3_normuon_scale(gp, FAKE, 8, FAKE, d.F16, 8 * 300, P2, -0.1, 1e-8, P2, None) == -1
+    assert L.dion3_normuon_scale(gp, FAKE, 8, FAKE, d.F16, 8 * 300, P2, 0.95, -1.0, P2, None) == -1
+    assert L.dion3_normuon_scale(gp, FAKE, 8, FAKE, d.BF16, 8 * 300, P2, 0.95, 1e-8, P2, None) == -1
+    assert L.dion3_normuon_scale(gp, FAKE, 8, FAKE, d.F16, 8 * 300 - 1, P2, 0.95, 1e-8, P2, None) == -1
+    # apply_rows_scaled: null W / idx / O, k, stride, dtype pair
+    assert L.dion3_apply_rows_scaled(gp, None, FAKE, FAKE, 8, FAKE, d.F16, 8 * 300, None, 0.1, 0.0, 0.9, None) == -1
+    assert L.dion3_apply_rows_scaled(gp, FAKE, FAKE, None, 8, FAKE, d.F16, 8 * 300, None, 0.1, 0.0, 0.9, None) == -1
+    assert L.dion3_apply_rows_scaled(gp, FAKE, FAKE, FAKE, 65, FAKE, d.F16, 65 * 300, None, 0.1, 0.0, 0.9,
+                                     None) == -1
+    assert L.dion3_apply_rows_scaled(gp, FAKE, FAKE, FAKE, 8, FAKE, d.F16, 100, None, 0.1, 0.0, 0.9, None) == -1
+    assert L.dion3_apply_rows_scaled(gp, FAKE, FAKE, FAKE, 8, FAKE, d.BF16, 8 * 300, None, 0.1, 0.0, 0.9,
+                                     None) == -1
+    # step_normuon: V missing (array or one entry), beta2, workspace
+    p = d.make_ns_params()
+    pp = ctypes.byref(p)
+    groups = (d.Group * 1)(g)
+    ks = (ctypes.c_int * 1)(16)
+    ptrs = (ctypes.c_void_p * 1)(0x1000)
+    vs = (ctypes.c_void_p * 1)(0x3000)
+    vnull = (ctypes.c_void_p * 1)(None)
+    sw = L.dion3_step_workspace_bytes(1, groups, ks, pp)
+    assert sw > 0
+    args = (ptrs, ptrs, ptrs, ks, ptrs)
+    assert L.dion3_step_normuon(1, groups, *args, None, 0, 0, pp, 0.1, 0.0, 0.9, 0.95, 1e-8, FAKE, sw, None) == -1
+    assert L.dion3_step_normuon(1, groups, *args, vnull, 0, 0, pp, 0.1, 0.0, 0.9, 0.95, 1e-8, FAKE, sw, None) == -1
+    assert L.dion3_step_normuon(1, groups, *args, vs, 0, 0, pp, 0.1, 0.0, 0.9, 2.0, 1e-8, FAKE, sw, None) == -1
+    assert L.dion3_step_normuon(1, groups, *args, vs, 0, 0, pp, 0.1, 0.0, 0.9, 0.95, 1e-8, FAKE, sw - 1,
+                                None) == -3
