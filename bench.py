@@ -123,7 +123,7 @@ def kernel_work(groups, ks, ns_bytes=2, store_bytes=2):
     return {name: (kind[name], v) for name, v in w.items()}
 
 
-def cpu_baseline(groups, ks, f, eta, set_name, budget_s=10.0, max_mats=4):
+def cpu_baseline(groups, ks, f, eta, set_name, budget_s=12.0, max_mats=12):
     """The oracle's whole step on matrices of the first shape group (attention
     projections) until about `budget_s` seconds have elapsed, scaled to the
     full set by parameter count."""
@@ -190,6 +190,17 @@ def run_step_bench(d, synth, torch, args):
     torch.cuda.synchronize()
     print("# warmup done", file=sys.stderr, flush=True)
 
+    # host time of one step: the wall time of the call that enqueues it (the
+    # queue is drained before each call, so nothing waits on the device)
+    host = []
+    for _ in range(5):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        one_step(True)
+        host.append(1e3 * (time.perf_counter() - t0))
+    torch.cuda.synchronize()
+    host_ms = sorted(host)[len(host) // 2]
+
     launches_per_step = 64
     d.dion3_timing_enable(launches_per_step * args.steps + 64)
     # one event between consecutive steps: the mean over the timed region and
@@ -228,6 +239,7 @@ def run_step_bench(d, synth, torch, args):
                        "achieved": round(ach, 2), "unit": unit, "frac": round(ach / peak, 4)}
     del plan, Ws, Ms, Gs, idxs, Vs
     torch.cuda.empty_cache()
+    pct["host"] = host_ms
     return ms, pct, table, groups, ks, eta
 
 
@@ -312,6 +324,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": False,
         "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "ms_per_step_p50": round(pct["p50"], 3), "ms_per_step_p90": round(pct["p90"], 3),
+        "host_ms_per_step": round(pct["host"], 3),
         "data": "synthetic (Gaussian gradients with log-normal line scales, seeded)",
         "config": {"workload": f"{args.set} shape set Dion3 step, f={args.f:g}"
                                + ("" if args.flavor == "muon" else ", NorMuon flavour"),
