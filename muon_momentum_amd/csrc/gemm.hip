@@ -835,8 +835,11 @@ static int launch_typed(const GemmArgs& a, hipStream_t s) {
   p.alpha = a.alpha; p.beta = a.beta; p.gamma = a.gamma;
 
   // The 256 x 256 tile is used for fp16 / bf16 when the shape is a whole
-  // number of tiles and there are at least two tiles per compute unit;
-  // otherwise (ragged shapes, small batches, fp32) the 128 x 128 tile.
+  // number of tiles and there are at least 128 of them (half the compute
+  // units; measured on MI355X, one 4096^2 symmetric product with 136 tiles
+  // runs faster on them than with 528 tiles of 128 x 128, one 2048^2 product
+  // with 36 does not); otherwise (ragged shapes, small batches, fp32) the
+  // 128 x 128 tile.
   auto tiles_for = [&](int bm, int& tm, int& tn) {
     tm = (a.M + bm - 1) / bm;
     tn = (a.N + bm - 1) / bm;
@@ -852,7 +855,7 @@ static int launch_typed(const GemmArgs& a, hipStream_t s) {
   // the large-tile kernel addresses each operand with 32-bit byte offsets
   const bool fits32 = (long long)a.M * a.lda * 2 < (1LL << 31) &&
                       (long long)(OP == OP_GEMM ? a.K : a.N) * a.ldb * 2 < (1LL << 31);
-  const bool big = HALF && fits32 && fast_for(256) && tiles_for(256, tm, tn) >= 512;
+  const bool big = HALF && fits32 && fast_for(256) && tiles_for(256, tm, tn) >= 128;
   const int bm = big ? 256 : BM;
   const long long grid = tiles_for(bm, tm, tn);
   p.tiles_m = tm;
