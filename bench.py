@@ -41,8 +41,8 @@ ETA0 = 0.02                      # eta at f = 1; eta = ETA0 / sqrt(f)
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--set", default="7b", choices=["1b", "7b", "14b"])
     ap.add_argument("--f", type=float, default=0.25)
     ap.add_argument("--flavor", default="muon", choices=["muon", "normuon"],
