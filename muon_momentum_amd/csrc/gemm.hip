@@ -16,8 +16,10 @@
 // on both operands makes the contraction exact for any chunk order.
 //   f16 / bf16: v_mfma_f32_32x32x16 (one MFMA per chunk pair)
 //   f32:        v_mfma_f32_32x32x2  (four MFMAs per chunk pair)
-// Accumulation is fp32; the epilogue applies alpha / beta / gamma in fp32 and
-// rounds once to the output type.
+// Accumulation is fp32; the epilogue applies alpha / beta / gamma in fp32 as
+// fma(beta, e, alpha acc) + gamma and rounds that fp32 value to the output
+// type, written out the same way in every kernel, so that a matrix's result
+// does not depend on the tile size its batch gets.
 #include <type_traits>
 
 #include "common.h"
@@ -116,9 +118,20 @@ __device__ __forceinline__ uint4 load_chunk(const T* base, long long ld, int row
   return u.v;
 }
 
+// The epilogue's fp32 value rounded to the output type.  The empty asm makes
+// the fp32 value opaque, so the compiler cannot fuse the multiply-add before
+// it and the rounding into one mixed-precision instruction (which rounds once,
+// from the exact value): it would do so on some code paths and not on others,
+// and the tile kernels would then disagree in the last bit.
+template <typename TO>
+__device__ __forceinline__ TO epi_round(float v) {
+  asm("" : "+v"(v));
+  return Store<TO>::from_f32(v);
+}
+
 template <typename TO>
 __device__ __forceinline__ void put(void* C, long long off, float v) {
-  ((TO*)C)[off] = Store<TO>::from_f32(v);
+  ((TO*)C)[off] = epi_round<TO>(v);
 }
 
 // OP: GemmOp.  BT: B operand is an N-contiguous K x N matrix (X in Q X) that
@@ -277,9 +290,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(KParams p) {
         if (diag && gi < gj) continue;                  // upper half of a diagonal tile
         float v = p.alpha * acc[i][j][r];
         if (OP == OP_SYRK) {
-          if (p.beta != 0.f) v += p.beta * Store<TO>::to_f32(E[(long long)gi * p.lde + gj]);
+          if (p.beta != 0.f) v = __builtin_fmaf(p.beta, Store<TO>::to_f32(E[(long long)gi * p.lde + gj]), v);
         } else if (OP == OP_SQ_ADD) {
-          v += p.beta * Store<TO>::to_f32(E[(long long)gi * p.lde + gj]);
+          v = __builtin_fmaf(p.beta, Store<TO>::to_f32(E[(long long)gi * p.lde + gj]), v);
           if (gi == gj) v += p.gamma;
         }
         put<TO>(C, (long long)gi * p.ldc + gj, v);
@@ -544,8 +557,8 @@ void gemm256_kernel(KParams p) {
               constexpr int g = decltype(gc)::value;
               static_for<2>([&](auto hc) {
                 constexpr int h = decltype(hc)::value;
-                const TO lo = Store<TO>::from_f32(p.alpha * acc_read(acc[i][j][4 * g + 2 * h]));
-                const TO hi = Store<TO>::from_f32(p.alpha * acc_read(acc[i][j][4 * g + 2 * h + 1]));
+                const TO lo = epi_round<TO>(p.alpha * acc_read(acc[i][j][4 * g + 2 * h]));
+                const TO hi = epi_round<TO>(p.alpha * acc_read(acc[i][j][4 * g + 2 * h + 1]));
                 d[g][h] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
                           ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
               });
@@ -734,7 +747,7 @@ void gemm256_kernel(KParams p) {
             if constexpr (HAS_E && sizeof(TO) == 2) {
               if (use_e) {
                 const uint16_t eb = (uint16_t)(ebits[q >> 1] >> (16 * (q & 1)));
-                v[q] += p.beta * Store<TO>::to_f32(__builtin_bit_cast(TO, eb));
+                v[q] = __builtin_fmaf(p.beta, Store<TO>::to_f32(__builtin_bit_cast(TO, eb)), v[q]);
               }
             }
           });
@@ -746,7 +759,7 @@ void gemm256_kernel(KParams p) {
             });
           }
           TO o[4];
-          static_for<4>([&](auto qc) { o[decltype(qc)::value] = Store<TO>::from_f32(v[decltype(qc)::value]); });
+          static_for<4>([&](auto qc) { o[decltype(qc)::value] = epi_round<TO>(v[decltype(qc)::value]); });
           TO* dst = cb + (long long)(32 * i + 8 * g) * p.ldc + 32 * j;
           if (!dblk) {
             static_for<4>([&](auto qc) { dst[(long long)decltype(qc)::value * p.ldc] = o[decltype(qc)::value]; });

@@ -366,3 +366,32 @@ def test_gemm_qx_large_tiles(d, dt, odt, b, k, m):
     for i in _sample(b):
         ref = to64(Q[i]) @ to64(X[i])
         assert rel_fro(to64(Y[i]), ref) <= TOL[odt if odt != "f32" else dt], i
+
+
+def test_products_independent_of_batch(d):
+    """Each matrix's product is the same bits whether it runs alone (128 x 128
+    tiles: too few tiles for the large kernel) or in a batch large enough for
+    the 256 x 256 tiles, so splitting a Newton-Schulz batch does not change
+    any result."""
+    g = torch.Generator(device="cpu").manual_seed(7)
+    n, m, b = 1024, 512, 16
+    X = (torch.randn(b, n, m, generator=g) / m ** 0.5).to(torch.float16).to(DEV)
+    Q = (torch.randn(b, n, n, generator=g) / n ** 0.5).to(torch.float16).to(DEV)
+    E = (torch.randn(b, n, n, generator=g) / n ** 0.5).to(torch.float16).to(DEV)
+    E = ((E + E.transpose(1, 2)) * 0.5).contiguous()
+    full = torch.empty(b, n, n, dtype=torch.float16, device=DEV)
+    one = torch.empty(1, n, n, dtype=torch.float16, device=DEV)
+    d.dion3_syrk(X, full, 0.5, 0.0)
+    d.dion3_syrk(X[3:4], one, 0.5, 0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(full[3].view(torch.int16), one[0].view(torch.int16)), "syrk"
+    d.dion3_sym_sq_add(E, E, full, -0.25, 0.75, 1.5)
+    d.dion3_sym_sq_add(E[3:4], E[3:4], one, -0.25, 0.75, 1.5)
+    torch.cuda.synchronize()
+    assert torch.equal(full[3].view(torch.int16), one[0].view(torch.int16)), "sym_sq_add"
+    Y = torch.empty(b, n, m, dtype=torch.float16, device=DEV)
+    Y1 = torch.empty(1, n, m, dtype=torch.float16, device=DEV)
+    d.dion3_gemm(Q, X, Y, 1.0)
+    d.dion3_gemm(Q[3:4], X[3:4], Y1, 1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(Y[3].view(torch.int16), Y1[0].view(torch.int16)), "gemm"

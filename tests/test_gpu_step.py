@@ -100,6 +100,30 @@ def test_multigroup_bf16_step_matches_manual_and_oracle(d, f):
             assert np.array_equal(bits(B[gi][0][j]), np_bits(Wg, torch.bfloat16))
 
 
+@pytest.mark.parametrize("shapes", [
+    [(256, 256, 2), (128, 512, 3), (512, 128, 2)],   # square matrices, then a class of two groups
+    [(128, 512, 3)],                                 # a single class
+    [(200, 96, 1), (128, 512, 1), (512, 128, 1)],    # single matrices, two of them in one class
+])
+def test_step_class_layouts_match_manual(d, shapes):
+    """Classes made of several groups, a single class, classes of single
+    matrices: the whole step equals the entry points run one class at a time."""
+    dt = "bf16"
+    mu, eta, wd = 0.95, 0.03, 0.01
+    params = d.make_ns_params(ns_dtype=d.F16)
+    ks = [d.dion3_k_from_fraction(min(r, c), 0.25) for r, c, _ in shapes]
+    A = _groups(shapes, dt, step=2, seed0=20)
+    B = [(W.clone(), M.clone(), G.clone()) for W, M, G in A]
+    idx_a = [torch.empty(b, k, dtype=torch.int32, device=DEV) for (_, _, b), k in zip(shapes, ks)]
+    d.dion3_step([g[0] for g in A], [g[1] for g in A], [g[2] for g in A], ks, idx_a, eta, wd, mu, params)
+    idx_b, _ = manual_step(d, B, ks, params, eta, wd, mu)
+    torch.cuda.synchronize()
+    for gi in range(len(shapes)):
+        assert np.array_equal(idx_a[gi].cpu().numpy(), idx_b[gi].cpu().numpy()), gi
+        assert np.array_equal(bits(A[gi][0]), bits(B[gi][0])), ("W", gi)
+        assert np.array_equal(bits(A[gi][1]), bits(B[gi][1])), ("M", gi)
+
+
 def test_step_deterministic(d):
     shapes = [(256, 768, 2), (768, 256, 1)]
     ks = [64, 64]
