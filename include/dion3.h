@@ -243,10 +243,11 @@ size_t dion3_step_workspace_bytes(int n_groups, const dion3_group* groups, const
  * dion3_apply_rows.  W[i], M[i], G[i] are the group tensors, idx[i] receives
  * the [batch][k[i]] selected indices.  eta, wd, mu as in dion3_apply_rows
  * (one value for all groups).
- * Streams: the first class's momentum pass and the last class's update are
- * enqueued on `stream`; the gathers and Newton-Schulz products run on a side
- * stream, and the other momentum passes and updates on a stream limited to
- * half of the compute units, so that they overlap another class's products.
+ * Streams: the first class's momentum pass and gather and the last class's
+ * update are enqueued on `stream`; the Newton-Schulz products run on a side
+ * stream, and the other momentum passes, gathers and updates on a stream
+ * limited to half of the compute units, so that they overlap another class's
+ * products.
  * The library streams belong to the current device; the library creates them
  * (with an event pool) on the device's first step and keeps them until the
  * process ends.  Graph capture is not supported: a call on a capturing stream
@@ -258,8 +259,9 @@ size_t dion3_step_workspace_bytes(int n_groups, const dion3_group* groups, const
  * current device.  Concurrent calls on one device are serialised while they
  * enqueue.  The workspace (dion3_step_workspace_bytes) holds the selected
  * sums of squares and the NorMuon row factors of every group and, with two or
- * more (k, m) classes, two
- * Newton-Schulz outputs so that one class's update overlaps the next class. */
+ * more (k, m) classes, two gathered inputs and two Newton-Schulz outputs, so
+ * that the next class's gather and this class's update overlap this class's
+ * products. */
 int dion3_step(int n_groups, const dion3_group* groups, void* const* W, void* const* M,
                const void* const* G, const int* k, int32_t* const* idx,
                const dion3_ns_params* p, float eta, float wd, float mu,

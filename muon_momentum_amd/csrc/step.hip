@@ -10,18 +10,21 @@
 // up-projection group (row selection) and a down-projection group (column
 // selection, stored transposed) run their Newton-Schulz together.
 //
-// Three streams.  The gathers and the matrix-core-bound Newton-Schulz chain
-// of each class run on a side stream owned by the library.  The first class's
-// momentum + selection pass and the last class's update have nothing to
-// overlap and run on the caller's stream over the whole chip; the momentum
-// passes of the other classes and the updates of all but the last run on a
-// second library stream restricted to half of the compute units (spread
-// evenly over the XCDs), so that these HBM-bound passes overlap the products
-// of another class without taking every compute unit from them.  Events order
-// the streams: class c's gather waits for its groups' selection, class c's
-// update for its Newton-Schulz, and the caller's stream ends the call having
-// waited for all library-stream work.  Every kernel computes exactly what it
-// computes on one stream, so the results do not depend on the overlap.
+// Three streams.  The matrix-core-bound Newton-Schulz chain of each class
+// runs on a side stream owned by the library.  The first class's momentum +
+// selection pass and its gather have nothing to overlap and run on the
+// caller's stream over the whole chip, and so does the last class's update;
+// the momentum passes and gathers of the other classes and the updates of all
+// but the last run on a second library stream restricted to half of the
+// compute units (spread evenly over the XCDs), in the order momentum and
+// gather of class c + 1, then update of class c, so that these HBM-bound
+// passes overlap the products of class c without taking every compute unit
+// from them.  Events order the streams: class c's Newton-Schulz waits for its
+// gather, class c's update for its Newton-Schulz, a gather for the end of the
+// Newton-Schulz that last read its buffer, and the caller's stream ends the
+// call having waited for all library-stream work.  Every kernel computes
+// exactly what it computes on one stream, so the results do not depend on
+// the overlap.
 #include <mutex>
 #include <vector>
 
@@ -36,7 +39,7 @@ struct Plan {
   std::vector<size_t> sqn_off;             // per group: offset of its [batch] fp64 slot
   std::vector<size_t> rs_off;              // per group: offset of its [batch][k] fp32 row factors
   size_t rowsel = 0, sqn = 0, rs = 0, xbuf = 0, gram = 0;
-  size_t bytes() const { return rowsel + sqn + rs + (classes.size() > 1 ? 3 : 2) * xbuf + gram; }
+  size_t bytes() const { return rowsel + sqn + rs + (classes.size() > 1 ? 4 : 2) * xbuf + gram; }
 };
 
 static bool make_plan(int ng, const dion3_group* g, const int* k, const dion3_ns_params* p, Plan& P) {
@@ -141,16 +144,19 @@ static int run_step(int n_groups, const dion3_group* groups, void* const* W, voi
   if (V && (!(beta2 >= 0.f && beta2 <= 1.f) || !(nm_eps >= 0.f))) return DION3_ERR_INVALID_ARG;
   if (!ws || ws_bytes < P.bytes()) return DION3_ERR_WORKSPACE;
   const int nc = (int)P.classes.size();
-  // workspace: top-k partials | per-group selected sums of squares | X0 |
-  // outputs of alternate classes (two while a class's update may still read
-  // the previous output) | Newton-Schulz scratch
+  // workspace: top-k partials | per-group selected sums of squares |
+  // NorMuon row factors | X0 of alternate classes (the next class is gathered
+  // while this one's products run) | outputs of alternate classes (a class's
+  // update may still read the previous output) | Newton-Schulz scratch
   char* base = (char*)ws;
   char* rs_ws = base;
   char* sqn_base = rs_ws + P.rowsel;
   char* rsc_base = sqn_base + P.sqn;
+  const int nx = nc > 1 ? 2 : 1;
   char* X0 = rsc_base + P.rs;
-  char* Obuf[2] = {X0 + P.xbuf, X0 + (nc > 1 ? 2 : 1) * P.xbuf};
-  char* gws = X0 + (nc > 1 ? 3 : 2) * P.xbuf;
+  char* X0buf[2] = {X0, X0 + (nx - 1) * P.xbuf};
+  char* Obuf[2] = {X0 + nx * P.xbuf, X0 + (2 * nx - 1) * P.xbuf};
+  char* gws = X0 + 2 * nx * P.xbuf;
   const size_t es = dtype_size(p->ns_dtype);
   hipStream_t s = (hipStream_t)stream;
 
@@ -172,55 +178,69 @@ static int run_step(int n_groups, const dion3_group* groups, void* const* W, voi
   hipEvent_t ev_side_end = ev_upd[nc + 1];      // side stream drained
   hipEvent_t ev_mem_end = ev_upd[nc + 2];       // overlapped stream drained
   auto hip_ok = [](hipError_t e) { return e == hipSuccess ? DION3_OK : DION3_ERR_HIP; };
-  // class c's momentum pass: the caller's stream for the first class, else the
-  // overlapped stream; class c's update: the caller's stream for the last
+  // class c's momentum + selection and gather: the caller's stream for the
+  // first class, else the overlapped stream; class c's update: the caller's
+  // stream for the last class, else the overlapped stream
   auto sel_stream = [&](int c) { return c == 0 ? s : mem; };
   auto upd_stream = [&](int c) { return c == nc - 1 ? s : mem; };
-
   bool used_side = false, used_mem = false;
-  for (int c = 0; c < nc && !st; ++c) {
+
+  // momentum + selection of class c, then the gather of its selected lines
+  // into X0buf[c & 1] (free once class c - 2's Newton-Schulz has ended)
+  auto select_and_gather = [&](int c) -> int {
     hipStream_t sc = sel_stream(c);
-    if (c == 1) {
-      st = hip_ok(hipEventRecord(ev_fork, s));
-      if (!st) st = hip_ok(hipStreamWaitEvent(mem, ev_fork, 0));
-      used_mem = used_mem || !st;
-      if (st) break;
-    }
-    for (int i : P.classes[c]) {
+    const auto& cls = P.classes[c];
+    const int kk = k[cls[0]], mm = P.m[cls[0]];
+    const size_t slice = (size_t)kk * mm * es;
+    int r = DION3_OK;
+    for (int i : cls) {
       const dion3_group& gi = groups[i];
       // deferred error feedback: idx[i] holds the previous selection on entry;
       // its decay is applied in this pass, then idx[i] is overwritten
-      st = dion3_momentum_rowsel_ef(&gi, M[i], G[i], k[i], idx[i], nullptr,
-                                    (double*)(sqn_base + P.sqn_off[i]),
-                                    deferred && has_prev ? idx[i] : nullptr, k[i], mu, rs_ws,
-                                    P.rowsel, sc);
-      if (st) break;
+      r = dion3_momentum_rowsel_ef(&gi, M[i], G[i], k[i], idx[i], nullptr, (double*)(sqn_base + P.sqn_off[i]),
+                                   deferred && has_prev ? idx[i] : nullptr, k[i], mu, rs_ws, P.rowsel, sc);
+      if (r) return r;
     }
-    if (!st) st = hip_ok(hipEventRecord(ev_sel[c], sc));
+    if (c >= 2 && (r = hip_ok(hipStreamWaitEvent(sc, ev_ns[c - 2], 0)))) return r;
+    int nb = 0;
+    for (int i : cls) {
+      const dion3_group& gi = groups[i];
+      r = dion3_gather_rows(&gi, M[i], idx[i], kk, (const double*)(sqn_base + P.sqn_off[i]), p->eps,
+                            p->ns_dtype, X0buf[c & 1] + nb * slice, sc);
+      if (r) return r;
+      nb += gi.batch;
+    }
+    return hip_ok(hipEventRecord(ev_sel[c], sc));
+  };
+
+  st = select_and_gather(0);
+  if (!st && nc > 1) {
+    // the overlapped stream starts once the first class is gathered
+    st = hip_ok(hipEventRecord(ev_fork, s));
+    if (!st) st = hip_ok(hipStreamWaitEvent(mem, ev_fork, 0));
+    used_mem = used_mem || !st;
   }
-  // per class: gather + Newton-Schulz on the side stream, then the update
   for (int c = 0; c < nc && !st; ++c) {
     const auto& cls = P.classes[c];
     const int kk = k[cls[0]], mm = P.m[cls[0]];
     const size_t slice = (size_t)kk * mm * es;
     char* O = Obuf[c & 1];
+    // Newton-Schulz of class c on the side stream
     st = hip_ok(hipStreamWaitEvent(side, ev_sel[c], 0));
     used_side = used_side || !st;
     // O is rewritten two classes later: wait until that class's update read it
     if (!st && c >= 2) st = hip_ok(hipStreamWaitEvent(side, ev_upd[c - 2], 0));
     int nb = 0;
-    for (int i : cls) {
-      if (st) break;
-      const dion3_group& gi = groups[i];
-      st = dion3_gather_rows(&gi, M[i], idx[i], kk, (const double*)(sqn_base + P.sqn_off[i]), p->eps,
-                             p->ns_dtype, X0 + nb * slice, side);
-      nb += gi.batch;
-    }
+    for (int i : cls) nb += groups[i].batch;
     // aspect ratio 1: standard Newton-Schulz on the symmetric kernels (fewer
     // launches, equal work); otherwise Gram Newton-Schulz
-    if (!st) st = mm == kk ? dion3_standard_ns(nb, kk, mm, p, X0, O, gws, P.gram, side)
-                           : dion3_gram_ns(nb, kk, mm, p, X0, O, gws, P.gram, side);
+    if (!st) st = mm == kk ? dion3_standard_ns(nb, kk, mm, p, X0buf[c & 1], O, gws, P.gram, side)
+                           : dion3_gram_ns(nb, kk, mm, p, X0buf[c & 1], O, gws, P.gram, side);
     if (!st) st = hip_ok(hipEventRecord(ev_ns[c], side));
+    // the next class's momentum and gather go ahead of this class's update
+    // on the overlapped stream, so that they run beside these products
+    if (!st && c + 1 < nc) st = select_and_gather(c + 1);
+    // the update of class c
     hipStream_t uc = upd_stream(c);
     if (!st) st = hip_ok(hipStreamWaitEvent(uc, ev_ns[c], 0));
     nb = 0;
