@@ -364,12 +364,26 @@ __device__ __forceinline__ int swz32(int row, int chunk) {
   return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
 }
 
-// Byte offset of element column n (a multiple of 4) of row kr in an
-// N-contiguous stage (32 rows of 256 elements, 512 bytes): 16-byte chunk n/8
-// sits at chunk (n/8) xor 2 (kr mod 4), so the four rows read by one
-// transposing LDS read phase fall in distinct 32-byte slots.
+// N-contiguous stage (32 rows of 256 elements, 512 bytes): 16-byte chunk ch
+// of row kr sits at slot nslot(kr, ch) = t(ch) xor 2 (kr mod 4), where t flips
+// bit 3 of ch when bit 1 is set (an involution).  A transposing LDS read phase
+// reads, per 32 lanes, four rows (kr mod 4 = 0..3) x four chunks (two pairs
+// 2 apart, from the two 16-lane halves): the xor 2 (kr mod 4) spreads one
+// half over 8 slots of a 128-byte bank cycle, and t moves the other half to
+// the other 8 slots of 256 bytes, so neither 32 nor 64 four-byte banks see a
+// conflict (measured on MI355X: the plain xor 2 (kr mod 4) made these reads
+// 2-way conflicted).
+__device__ __forceinline__ int nslot(int kr, int ch) {
+  return (ch ^ (((ch >> 1) & 1) << 3)) ^ (2 * (kr & 3));
+}
+// the chunk that belongs in slot s of row kr (the inverse of nslot)
+__device__ __forceinline__ int nchunk(int kr, int s) {
+  const int u = s ^ (2 * (kr & 3));
+  return u ^ (((u >> 1) & 1) << 3);
+}
+// Byte offset of element column n (a multiple of 4) of row kr.
 __device__ __forceinline__ int swzn(int kr, int n) {
-  return kr * 512 + ((((n >> 3) ^ (2 * (kr & 3)))) << 4) + ((n & 4) << 1);
+  return kr * 512 + (nslot(kr, n >> 3) << 4) + ((n & 4) << 1);
 }
 
 // Wait until at most n vector memory operations of this wave are outstanding
@@ -464,7 +478,7 @@ void gemm256_kernel(KParams p) {
     kb = 64 * (int)p.ldb * 2;
   } else {
     const int kr = 2 * wave + (lane >> 5);
-    vb = (kr * (int)p.ldb + (((lane & 31) ^ (2 * (kr & 3))) << 3)) * 2;
+    vb = (kr * (int)p.ldb + (nchunk(kr, lane & 31) << 3)) * 2;
     kb = 8 * (int)p.ldb * 2;                          // +8 rows per instruction
   }
   auto tile_addr = [&](int L, TileAddr& a) {
