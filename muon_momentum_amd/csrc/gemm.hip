@@ -387,20 +387,24 @@ __device__ __forceinline__ int swzn(int kr, int n) {
 }
 
 // Wait until at most n vector memory operations of this wave are outstanding
-// (n: a multiple of 8 up to 56; 8 DMA instructions per stage, 32 stores per
-// tile epilogue).  The counter retires loads and stores in issue order.
+// (0 <= n <= 63, the counter's range; larger n waits as for 63).  The counter
+// retires loads and stores in issue order.
+#define DION3_VM_CASE(k) \
+  case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
+#define DION3_VM_CASE8(k) DION3_VM_CASE(k) DION3_VM_CASE(k + 1) DION3_VM_CASE(k + 2) DION3_VM_CASE(k + 3) \
+  DION3_VM_CASE(k + 4) DION3_VM_CASE(k + 5) DION3_VM_CASE(k + 6) DION3_VM_CASE(k + 7)
 __device__ __forceinline__ void wait_vm(int n) {
   switch (n) {
-    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
-    case 16: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
-    case 24: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
-    case 32: asm volatile("s_waitcnt vmcnt(32)" ::: "memory"); break;
-    case 40: asm volatile("s_waitcnt vmcnt(40)" ::: "memory"); break;
-    case 48: asm volatile("s_waitcnt vmcnt(48)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    DION3_VM_CASE8(0) DION3_VM_CASE8(8) DION3_VM_CASE8(16) DION3_VM_CASE8(24)
+    DION3_VM_CASE8(32) DION3_VM_CASE8(40) DION3_VM_CASE8(48) DION3_VM_CASE8(56)
+    default:
+      if (n > 63) asm volatile("s_waitcnt vmcnt(63)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      break;
   }
 }
+#undef DION3_VM_CASE8
+#undef DION3_VM_CASE
 
 typedef short short4v __attribute__((ext_vector_type(4)));
 
@@ -440,8 +444,8 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
 void gemm256_kernel(KParams p) {
   constexpr bool SYM = OP != OP_GEMM;
   constexpr bool BT = OP == OP_GEMM;
-  constexpr bool SWAP = OP == OP_GEMM;              // MFMA produces C^T blocks
-  constexpr bool MULTI = SWAP && sizeof(TO) == 2;   // several tiles per work-group
+  constexpr bool SWAP = true;                       // MFMA produces C^T blocks
+  constexpr bool MULTI = sizeof(TO) == 2;           // several tiles per work-group
   constexpr int BM = 256, BN = 256;
   constexpr int BK = 32;                      // K elements per stage
   constexpr int WT = 128;                     // wave tile edge
@@ -596,6 +600,141 @@ void gemm256_kernel(KParams p) {
     }
   };
 
+  const bool use_e = OP == OP_SQ_ADD || (OP == OP_SYRK && p.beta != 0.f);
+
+  // Symmetric epilogue (several tiles per work-group, no LDS).  Block (i, j)
+  // of the wave holds C[r][c] for r = lane%32 and c = 8 g + 4 (lane/32) + q in
+  // acc[i][j][4 g + q] (the Q X layout).  Direct part: the Q X stores, 16-byte
+  // chunks of row r.  Mirror part: in each group of 8 lanes (rows 8 o .. 8 o + 7
+  // of the block), a butterfly transpose of the 8 packed dwords over lane
+  // distances 4, 2, 1 leaves lane t = lane%8 the 8 rows of columns
+  // c0 = 8 (t/2) + 4 (lane/32) + 2 (t mod 2) and c0 + 1, which are 16-byte
+  // chunks of rows c0 and c0 + 1 of the transposed position.  Diagonal tiles:
+  // the wave above the diagonal writes nothing (its quadrant is the mirror of
+  // the one below), blocks above the diagonal of the two diagonal quadrants
+  // likewise, and on a diagonal block the direct chunk keeps columns <= row
+  // and the mirror chunk rows > column, so every entry is written once, from
+  // the value computed at or below the diagonal.  The epilogue operand is read
+  // at the direct position and waited for before any store.  Returns the
+  // number of stores every lane issues (a lower bound of the wave's count).
+  auto epilogue_sym = [&](const TileAddr& a) -> int {
+    int nst = 0;
+    if constexpr (SYM) {
+      const bool diag_tile = a.ti == a.tj;
+      if (diag_tile && wm < wn) return 0;
+      const bool dq = diag_tile && wm == wn;
+      TO* C = (TO*)p.C + a.bat * p.sC;
+      const TO* E = (const TO*)p.E + (p.E ? a.bat * p.sE : 0);
+      const int lc = lane & 31, lh = lane >> 5;
+      const int o = lc >> 3, t = lc & 7;
+      const long long rb0 = a.m0 + wm * WT;       // first C row of the quadrant
+      const long long cb0 = a.n0 + wn * WT;       // first C column of the quadrant
+      uint2 epk[SUB][SUB][4];
+      if (use_e) {
+        static_for<SUB>([&](auto ic) {
+          static_for<SUB>([&](auto jc) {
+            constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
+            if (dq && i < j) return;
+            const TO* er = E + (rb0 + 32 * i + lc) * p.lde + cb0 + 32 * j + 4 * lh;
+            static_for<4>([&](auto gc) {
+              constexpr int g = decltype(gc)::value;
+              epk[i][j][g] = *(const uint2*)(er + 8 * g);
+            });
+          });
+        });
+        wait_vm(0);
+      }
+      static_for<SUB>([&](auto ic) {
+        static_for<SUB>([&](auto jc) {
+          constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
+          if (dq && i < j) return;
+          const bool dblk = dq && i == j;
+          __builtin_amdgcn_sched_barrier(0);
+          // packed results: dword 2 g + h holds columns 8 g + 4 (lane/32) + 2 h, + 1
+          uint32_t d[8];
+          static_for<4>([&](auto gc) {
+            constexpr int g = decltype(gc)::value;
+            static_for<2>([&](auto hc) {
+              constexpr int h = decltype(hc)::value;
+              float v0 = p.alpha * acc_read(acc[i][j][4 * g + 2 * h]);
+              float v1 = p.alpha * acc_read(acc[i][j][4 * g + 2 * h + 1]);
+              if (use_e) {
+                const uint32_t ew = h ? epk[i][j][g].y : epk[i][j][g].x;
+                v0 = __builtin_fmaf(p.beta, Store<TO>::to_f32(__builtin_bit_cast(TO, (uint16_t)(ew & 0xffffu))), v0);
+                v1 = __builtin_fmaf(p.beta, Store<TO>::to_f32(__builtin_bit_cast(TO, (uint16_t)(ew >> 16))), v1);
+              }
+              if (OP == OP_SQ_ADD && dblk) {
+                if (8 * g + 4 * lh + 2 * h == lc) v0 += p.gamma;
+                if (8 * g + 4 * lh + 2 * h + 1 == lc) v1 += p.gamma;
+              }
+              d[2 * g + h] = (uint32_t)__builtin_bit_cast(uint16_t, epi_round<TO>(v0)) |
+                             ((uint32_t)__builtin_bit_cast(uint16_t, epi_round<TO>(v1)) << 16);
+            });
+          });
+          // direct: lane L < 32 columns 16 pr .. + 7, lane L + 32 columns 16 pr + 8 .. + 15
+          TO* drow = C + (rb0 + 32 * i + lc) * p.ldc + cb0 + 32 * j;
+          static_for<2>([&](auto pc) {
+            constexpr int pr = decltype(pc)::value;
+            const auto s0 = __builtin_amdgcn_permlane32_swap(d[4 * pr], d[4 * pr + 2], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(d[4 * pr + 1], d[4 * pr + 3], false, false);
+            const uint4 w = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+            const int y0 = 16 * pr + 8 * lh;
+            TO* dst = drow + y0;
+            if (!dblk || y0 + 7 <= lc) {
+              *(uint4*)dst = w;
+            } else if (y0 <= lc) {
+              union { uint4 v; TO e[8]; } u;
+              u.v = w;
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if (y0 + e <= lc) dst[e] = u.e[e];
+            }
+          });
+          // mirror: transpose the 8 dwords across the 8 lanes of the group
+          static_for<3>([&](auto sc) {
+            constexpr int s = 4 >> decltype(sc)::value;
+            const bool up = (t & s) != 0;
+            static_for<8>([&](auto kc) {
+              constexpr int k = decltype(kc)::value;
+              if constexpr ((k & s) == 0) {
+                constexpr int kk = k | s;
+                const uint32_t send = up ? d[k] : d[kk];
+                const uint32_t recv =
+                    (uint32_t)__builtin_amdgcn_ds_swizzle((int)send, (s << 10) | 0x1f);
+                if (up) d[k] = recv;
+                else d[kk] = recv;
+              }
+            });
+          });
+          // dword k now holds row 8 o + k, columns c0 (low half) and c0 + 1
+          const uint4 ma = make_uint4((d[0] & 0xffffu) | (d[1] << 16), (d[2] & 0xffffu) | (d[3] << 16),
+                                      (d[4] & 0xffffu) | (d[5] << 16), (d[6] & 0xffffu) | (d[7] << 16));
+          const uint4 mb = make_uint4((d[0] >> 16) | (d[1] & 0xffff0000u), (d[2] >> 16) | (d[3] & 0xffff0000u),
+                                      (d[4] >> 16) | (d[5] & 0xffff0000u), (d[6] >> 16) | (d[7] & 0xffff0000u));
+          const int c0 = 8 * (t >> 1) + 4 * lh + 2 * (t & 1);
+          TO* mrow = C + (cb0 + 32 * j + c0) * p.ldc + rb0 + 32 * i + 8 * o;
+          static_for<2>([&](auto bc) {
+            constexpr int b = decltype(bc)::value;
+            const uint4& w = b ? mb : ma;
+            const int y = c0 + b;                 // block column = transposed row
+            TO* dst = mrow + b * p.ldc;
+            if (!dblk || 8 * o > y) {
+              *(uint4*)dst = w;
+            } else if (8 * o + 7 > y) {
+              union { uint4 v; TO e[8]; } u;
+              u.v = w;
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if (8 * o + e > y) dst[e] = u.e[e];
+            }
+          });
+          if (!dblk) nst += 4;
+        });
+      });
+    }
+    return nst;
+  };
+
   TileAddr cur, nxt;
   tile_addr(id, cur);
   if (MULTI && nt > 1) tile_addr(id + G, nxt);
@@ -619,6 +758,7 @@ void gemm256_kernel(KParams p) {
   // the vector memory queue never stalls the wave), then reads two fragments
   // of the next k-step (B fragments first), then runs its 4 MFMAs.
   int g = 0;                                  // global stage
+  int epi_st = 0;                             // stores of the previous tile's epilogue (per lane)
   // FIRST: a tile's first stage (its first k-step starts the accumulators);
   // LAST: a tile's last stage, which leaves the next stage's fragments unread
   // so that the epilogue runs with them dead (they are read after it)
@@ -668,8 +808,8 @@ void gemm256_kernel(KParams p) {
       // after stage g + 2's loads (the first two stages of a tile)
       const int last_issued = g + NBUF - 1 < GT ? g + NBUF - 1 : GT - 1;
       int allowed = g + 2 < GT ? 8 * (last_issued - (g + 2)) : 0;
-      if (MULTI && g + 2 < GT && j > 0 && kt < 2) allowed += kEpiStores;
-      wait_vm(allowed);
+      if (MULTI && g + 2 < GT && j > 0 && kt < 2) allowed += epi_st;
+      wait_vm(allowed < 63 ? allowed : 63);
       __syncthreads();
     }
     ++g;
@@ -682,7 +822,12 @@ void gemm256_kernel(KParams p) {
     if constexpr (MULTI) {
       // the finished tile's stores stay in flight while the next tile, whose
       // first stages are already loaded, computes
-      epilogue_swap(cur);
+      if constexpr (SYM) {
+        epi_st = epilogue_sym(cur);
+      } else {
+        epilogue_swap(cur);
+        epi_st = kEpiStores;
+      }
       // the next tile's first fragments (after the last tile: an in-bounds
       // read of a buffer no load is writing, unused)
 #pragma unroll
@@ -694,131 +839,10 @@ void gemm256_kernel(KParams p) {
     }
   }
 
-  if constexpr (SWAP) {
-    if constexpr (!MULTI) epilogue_swap(cur);
-    return;
-  }
-
-  // ---- symmetric epilogue (one tile per work-group).  Direct tile: each
-  // lane stores its values at C[gi][gj].  Mirror: the values are also written
-  // transposed into LDS, then copied out as whole 512-byte rows to C[gj][gi];
-  // on diagonal tiles only the strict upper part is copied, so every entry is
-  // written once.
-  const int m0 = cur.m0, n0 = cur.n0;
-  TO* C = (TO*)p.C + cur.bat * p.sC;
-  const TO* E = (const TO*)p.E + (p.E ? cur.bat * p.sE : 0);
-  const bool diag_tile = SYM && cur.ti == cur.tj;
-  const bool upper_wave = diag_tile && wm < wn;   // the mirror of the lower quadrant
-  constexpr bool HAS_E = OP == OP_SQ_ADD || OP == OP_SYRK;
-  const bool use_e = OP == OP_SQ_ADD || (OP == OP_SYRK && p.beta != 0.f);
-  // The epilogue operand is symmetric, so the four values E[gi..gi+3][gj] this
-  // lane needs per group are E[gj][gi..gi+3]: one 8-byte load.  All of them are
-  // issued before any store (the memory counter also counts stores).
-  uint2 epk[SUB][SUB][4];
-  if constexpr (HAS_E) {
-    if (use_e && !upper_wave) {
-      static_for<SUB>([&](auto ic) {
-        static_for<SUB>([&](auto jc) {
-          constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
-          const int gi0 = m0 + wm * WT + i * 32;
-          const int gj0 = n0 + wn * WT + j * 32;
-          if (gi0 < gj0) return;
-          const int gj = gj0 + (lane & 31);
-          static_for<4>([&](auto gc) {
-            constexpr int g = decltype(gc)::value;
-            const int gib = gi0 + 8 * g + 4 * (lane >> 5);
-            epk[i][j][g] = *(const uint2*)(E + (long long)gj * p.lde + gib);
-          });
-        });
-      });
-    }
-  }
-  // transposed tile in LDS: row c = gj - n0 (256 rows of 512 bytes), 8-byte
-  // granule r/4 of r = gi - m0 at position (r/4) xor (c mod 32)
-  char* tl = smem;
-  if (SYM) __syncthreads();                      // the last stage's LDS reads are done
-  asm volatile("" ::: "memory");
-  // per-lane bases: element (32 i + 8 g + q, 32 j) of this wave's quadrant
-  const int lc = lane & 31, lh = lane >> 5;
-  TO* cb = C + (long long)(m0 + wm * WT + 4 * lh) * p.ldc + (n0 + wn * WT + lc);
-  char* tb = tl + (wn * WT + lc) * 512;
-  if (!upper_wave) {
-    static_for<SUB>([&](auto ic) {
-      static_for<SUB>([&](auto jc) {
-        constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
-        const int gi0 = m0 + wm * WT + i * 32;
-        const int gj0 = n0 + wn * WT + j * 32;
-        if (SYM && gi0 < gj0) return;            // above the diagonal (diagonal tiles only)
-        const bool dblk = SYM && gi0 == gj0;     // a 32 x 32 block on the diagonal
-        static_for<4>([&](auto gc) {
-          constexpr int g = decltype(gc)::value;
-          uint32_t ebits[2] = {0u, 0u};
-          if constexpr (HAS_E && sizeof(TO) == 2) { ebits[0] = epk[i][j][g].x; ebits[1] = epk[i][j][g].y; }
-          float v[4];
-          static_for<4>([&](auto qc) {
-            constexpr int q = decltype(qc)::value;
-            v[q] = p.alpha * acc[i][j][4 * g + q];
-            if constexpr (HAS_E && sizeof(TO) == 2) {
-              if (use_e) {
-                const uint16_t eb = (uint16_t)(ebits[q >> 1] >> (16 * (q & 1)));
-                v[q] = __builtin_fmaf(p.beta, Store<TO>::to_f32(__builtin_bit_cast(TO, eb)), v[q]);
-              }
-            }
-          });
-          if (OP == OP_SQ_ADD && dblk) {
-            // gi == gj: row 8 g + 4 lh + q of the block equals column lc
-            static_for<4>([&](auto qc) {
-              constexpr int q = decltype(qc)::value;
-              if (8 * g + 4 * lh + q == lc) v[q] += p.gamma;
-            });
-          }
-          TO o[4];
-          static_for<4>([&](auto qc) { o[decltype(qc)::value] = epi_round<TO>(v[decltype(qc)::value]); });
-          TO* dst = cb + (long long)(32 * i + 8 * g) * p.ldc + 32 * j;
-          if (!dblk) {
-            static_for<4>([&](auto qc) { dst[(long long)decltype(qc)::value * p.ldc] = o[decltype(qc)::value]; });
-          } else {
-            static_for<4>([&](auto qc) {
-              constexpr int q = decltype(qc)::value;
-              if (8 * g + 4 * lh + q >= lc) dst[(long long)q * p.ldc] = o[q];
-            });
-          }
-          if constexpr (SYM && sizeof(TO) == 2) {
-            const uint2 pk = make_uint2(
-                (uint32_t)__builtin_bit_cast(uint16_t, o[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, o[1]) << 16),
-                (uint32_t)__builtin_bit_cast(uint16_t, o[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, o[3]) << 16));
-            const int r4 = wm * 32 + i * 8 + 2 * g + lh;     // (gi - m0) / 4
-            *(uint2*)(tb + j * 32 * 512 + ((r4 ^ lc) << 3)) = pk;
-          }
-        });
-      });
-    });
-  }
-  if constexpr (SYM) {
-    __syncthreads();
-    // copy: thread t takes 16-byte chunk u = t mod 32 of rows t/32 + 8 s
-    const int u = tid & 31;
-#pragma unroll 4
-    for (int s = 0; s < 32; ++s) {
-      const int c = (tid >> 5) + 8 * s;
-      const int x = c & 31;
-      uint4 v = *(const uint4*)(tl + c * 512 + ((u ^ (x >> 1)) << 4));
-      if (x & 1) v = make_uint4(v.z, v.w, v.x, v.y);
-      TO* dst = C + (long long)(n0 + c) * p.ldc + m0 + 8 * u;
-      if (!diag_tile || 8 * u > c) {
-        *(uint4*)dst = v;
-      } else if (8 * u + 7 > c) {
-        union { uint4 v; TO e[8]; } w;
-        w.v = v;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (8 * u + e > c) dst[e] = w.e[e];
-      }
-    }
-  }
+  if constexpr (!MULTI) epilogue_swap(cur);
 }
 
-// Tiles per work-group for the multi-tile Q X kernel.  A work-group pays the
+// Tiles per work-group for the multi-tile large-tile kernel.  A work-group pays the
 // first stages' load latency once and then runs its tiles back to back; with
 // T tiles per work-group the launch takes ceil(ceil(n / T) / CUs) rounds of
 // T tiles.  The choice minimises rounds x (T x tile + start-up), with a tile
@@ -892,7 +916,7 @@ static int launch_typed(const GemmArgs& a, hipStream_t s) {
   p.ntiles = (int)grid;
   p.tiles_per_wg = 1;
   long long wgs = grid;
-  if constexpr (OP == OP_GEMM && sizeof(TO) == 2) {
+  if constexpr (sizeof(TO) == 2) {
     if (big && a.K / 32 >= kStages) wgs = multi_tile_grid(grid, a.K / 32, p.tiles_per_wg);
   }
 

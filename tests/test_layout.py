@@ -74,3 +74,91 @@ def test_plain_xor_layout_conflicts_on_64_banks():
         assert max(worst_conflict(read_addrs(0, j, 0, 0), 32, 64) for j in range(4)) == 2
     finally:
         t = saved
+
+
+# ---------------------------------------------------------------------------
+# Symmetric epilogue of the 256 x 256 kernel (gemm.hip: epilogue_sym): which
+# entry of C each lane stores, modelled from the accumulator layout.
+
+
+def _acc(m0, n0, wm, wn, i, j, lane, g, q):
+    """(row, column) of C held by accumulator 4 g + q of block (i, j)."""
+    lc, lh = lane & 31, lane >> 5
+    return (m0 + wm * 128 + 32 * i + lc, n0 + wn * 128 + 32 * j + 8 * g + 4 * lh + q)
+
+
+def _butterfly(X):
+    """Transpose of 8 dwords across each group of 8 lanes (distances 4, 2, 1)."""
+    for s in (4, 2, 1):
+        new = [list(r) for r in X]
+        for lane in range(64):
+            up = (lane & 7) & s
+            partner = lane ^ s
+            for k in range(8):
+                if k & s:
+                    continue
+                kk = k | s
+                sent = X[partner][k] if ((partner & 7) & s) else X[partner][kk]
+                if up:
+                    new[lane][k] = sent
+                else:
+                    new[lane][kk] = sent
+        X = new
+    return X
+
+
+def _symmetric_epilogue_writes(n):
+    written = {}
+    T = n // 256
+    for ti in range(T):
+        for tj in range(ti + 1):
+            m0, n0, diag = 256 * ti, 256 * tj, ti == tj
+            for wm in range(2):
+                for wn in range(2):
+                    if diag and wm < wn:
+                        continue
+                    dq = diag and wm == wn
+                    for i in range(4):
+                        for j in range(4):
+                            if dq and i < j:
+                                continue
+                            dblk = dq and i == j
+                            # direct: lane L < 32 columns 16 pr .. +7, lane L + 32 columns 16 pr + 8 .. +15
+                            for lane in range(64):
+                                lc, lh = lane & 31, lane >> 5
+                                for pr in range(2):
+                                    y0 = 16 * pr + 8 * lh
+                                    for e in range(8):
+                                        y = y0 + e
+                                        src = _acc(m0, n0, wm, wn, i, j, 32 * ((y % 8) // 4) + lc, y // 8, y % 4)
+                                        if dblk and y > lc:
+                                            continue
+                                        pos = (m0 + wm * 128 + 32 * i + lc, n0 + wn * 128 + 32 * j + y)
+                                        assert pos not in written
+                                        written[pos] = src
+                            # mirror
+                            d = [[(_acc(m0, n0, wm, wn, i, j, L, k >> 1, 2 * (k & 1)),
+                                   _acc(m0, n0, wm, wn, i, j, L, k >> 1, 2 * (k & 1) + 1)) for k in range(8)]
+                                 for L in range(64)]
+                            Y = _butterfly(d)
+                            for lane in range(64):
+                                lc, lh = lane & 31, lane >> 5
+                                o, t = lc >> 3, lc & 7
+                                c0 = 8 * (t >> 1) + 4 * lh + 2 * (t & 1)
+                                for b in range(2):
+                                    for e in range(8):
+                                        if dblk and not (8 * o + e > c0 + b):
+                                            continue
+                                        pos = (n0 + wn * 128 + 32 * j + c0 + b, m0 + wm * 128 + 32 * i + 8 * o + e)
+                                        assert pos not in written
+                                        written[pos] = Y[lane][e][b]
+    return written
+
+
+def test_symmetric_epilogue_writes_every_entry_once_from_the_lower_triangle():
+    for n in (256, 768):
+        w = _symmetric_epilogue_writes(n)
+        assert len(w) == n * n
+        for (x, y), (r, c) in w.items():
+            assert r >= c                      # computed at or below the diagonal
+            assert (x, y) in ((r, c), (c, r))  # stored at its place or the mirrored one
