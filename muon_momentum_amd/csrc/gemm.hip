@@ -762,12 +762,15 @@ void gemm256_kernel(KParams p) {
   // FIRST: a tile's first stage (its first k-step starts the accumulators);
   // LAST: a tile's last stage, which leaves the next stage's fragments unread
   // so that the epilogue runs with them dead (they are read after it)
-  auto stage = [&](auto first_c, auto last_c, int j, int kt) {
+  // ISS: 1 when the stage NBUF - 1 ahead exists (no test in the loop body),
+  // 0 when it does not, 2 to test at run time
+  auto stage = [&](auto first_c, auto last_c, auto iss_c, int j, int kt) {
     constexpr bool FIRST = decltype(first_c)::value;
     constexpr bool LAST = decltype(last_c)::value;
+    constexpr int ISS = decltype(iss_c)::value;
     // the stage NBUF - 1 ahead: this tile's, or the next tile's first ones
     const bool to_next = MULTI && kt + NBUF - 1 >= KT;
-    const bool iss = g + NBUF - 1 < GT;
+    const bool iss = ISS == 1 || (ISS == 2 && g + NBUF - 1 < GT);
     const int ls = kt + NBUF - 1 >= KT ? kt + NBUF - 1 - KT : kt + NBUF - 1;
     const int ib = (g + NBUF - 1) % NBUF;
     int4v ira = cur.ra, irb = cur.rb;
@@ -802,7 +805,17 @@ void gemm256_kernel(KParams p) {
       }
     });
     __builtin_amdgcn_sched_barrier(0);
-    if (g + 1 < GT) {
+    if constexpr (ISS == 1) {
+      // stages g + 3 .. g + NBUF - 1 are issued and may fly on (a constant
+      // count), and in a tile's first stages the previous epilogue's stores
+      if (MULTI && j > 0 && kt < 2) {
+        const int allowed = 8 * (NBUF - 3) + epi_st;
+        wait_vm(allowed < 63 ? allowed : 63);
+      } else {
+        wait_vm(8 * (NBUF - 3));
+      }
+      __syncthreads();
+    } else if (g + 1 < GT) {
       // stage g + 2 must land before this barrier; later stages may fly on,
       // and so may the previous tile's epilogue stores when they were issued
       // after stage g + 2's loads (the first two stages of a tile)
@@ -816,9 +829,17 @@ void gemm256_kernel(KParams p) {
   };
   using T1 = std::true_type;
   using T0 = std::false_type;
+  using IssYes = std::integral_constant<int, 1>;
+  using IssNo = std::integral_constant<int, 0>;
+  using IssTest = std::integral_constant<int, 2>;
   for (int j = 0; j < nt; ++j) {
-    stage(T1{}, T0{}, j, 0);
-    for (int kt = 1; kt < KT; ++kt) stage(T0{}, T0{}, j, kt);
+    stage(T1{}, T0{}, IssTest{}, j, 0);
+    // stages whose look-ahead exists: all of a tile followed by another
+    // (KT >= NBUF then), else those before the last NBUF - 1
+    const int kt_iss = j + 1 < nt ? KT : KT - (NBUF - 1);
+    int kt = 1;
+    for (; kt < kt_iss; ++kt) stage(T0{}, T0{}, IssYes{}, j, kt);
+    for (; kt < KT; ++kt) stage(T0{}, T0{}, IssNo{}, j, kt);
     if constexpr (MULTI) {
       // the finished tile's stores stay in flight while the next tile, whose
       // first stages are already loaded, computes
