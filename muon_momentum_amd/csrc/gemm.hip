@@ -524,15 +524,15 @@ void gemm256_kernel(KParams p) {
     }
   };
 
-  // fragments of one k-step (16 K elements) of global stage g: A rows
-  // wm*128 + 32 i + lane%32; B either likewise (K-contiguous) or through
-  // transposing reads (Q X)
-  auto read_a = [&](uint4& f, int g, int st, int i) {
-    const unsigned buf = lds0 + (unsigned)((g % NBUF) * STAGE);
+  // fragments of one k-step (16 K elements) of the stage in LDS buffer b:
+  // A rows wm*128 + 32 i + lane%32; B either likewise (K-contiguous) or
+  // through transposing reads (Q X)
+  auto read_a = [&](uint4& f, int b, int st, int i) {
+    const unsigned buf = lds0 + (unsigned)(b * STAGE);
     f = lds_read16(buf + swz32(wm * WT + i * 32 + (lane & 31), 2 * st + (lane >> 5)));
   };
-  auto read_b = [&](uint4& f, int g, int st, int j) {
-    const unsigned buf = lds0 + (unsigned)((g % NBUF) * STAGE) + 16384;
+  auto read_b = [&](uint4& f, int b, int st, int j) {
+    const unsigned buf = lds0 + (unsigned)(b * STAGE) + 16384;
     if (!BT) {
       f = lds_read16(buf + swz32(wn * WT + j * 32 + (lane & 31), 2 * st + (lane >> 5)));
     } else {
@@ -758,6 +758,7 @@ void gemm256_kernel(KParams p) {
   // the vector memory queue never stalls the wave), then reads two fragments
   // of the next k-step (B fragments first), then runs its 4 MFMAs.
   int g = 0;                                  // global stage
+  int bcur = 0;                               // its LDS buffer, g mod NBUF
   int epi_st = 0;                             // stores of the previous tile's epilogue (per lane)
   // FIRST: a tile's first stage (its first k-step starts the accumulators);
   // LAST: a tile's last stage, which leaves the next stage's fragments unread
@@ -772,7 +773,11 @@ void gemm256_kernel(KParams p) {
     const bool to_next = MULTI && kt + NBUF - 1 >= KT;
     const bool iss = ISS == 1 || (ISS == 2 && g + NBUF - 1 < GT);
     const int ls = kt + NBUF - 1 >= KT ? kt + NBUF - 1 - KT : kt + NBUF - 1;
-    const int ib = (g + NBUF - 1) % NBUF;
+    // LDS buffers (global stage mod NBUF, kept as running indices): this
+    // stage's, the next stage's, and the look-ahead stage's (the buffer the
+    // previous stage used)
+    const int bnext = bcur == NBUF - 1 ? 0 : bcur + 1;
+    const int ib = bcur == 0 ? NBUF - 1 : bcur - 1;
     int4v ira = cur.ra, irb = cur.rb;
     if (to_next) { ira = nxt.ra; irb = nxt.rb; }
     static_for<2 * SUB>([&](auto gxc) {
@@ -782,7 +787,7 @@ void gemm256_kernel(KParams p) {
       if (iss) dma(ira, irb, ls, ib, gx);
       // next k-step: step 1 of this stage, or step 0 of the next stage
       if (!(LAST && st == 1)) {
-        const int ns = st == 0 ? g : g + 1;
+        const int ns = st == 0 ? bcur : bnext;
         const int nst = st == 0 ? 1 : 0;
         uint4 (&na)[SUB] = st == 0 ? fa1 : fa0;
         uint4 (&nb)[SUB] = st == 0 ? fb1 : fb0;
@@ -826,6 +831,7 @@ void gemm256_kernel(KParams p) {
       __syncthreads();
     }
     ++g;
+    bcur = bnext;
   };
   using T1 = std::true_type;
   using T0 = std::false_type;
@@ -852,7 +858,7 @@ void gemm256_kernel(KParams p) {
       // the next tile's first fragments (after the last tile: an in-bounds
       // read of a buffer no load is writing, unused)
 #pragma unroll
-      for (int i = 0; i < SUB; ++i) { read_a(fa0[i], g, 0, i); read_b(fb0[i], g, 0, i); }
+      for (int i = 0; i < SUB; ++i) { read_a(fa0[i], bcur, 0, i); read_b(fb0[i], bcur, 0, i); }
       if (j + 1 < nt) {
         cur = nxt;
         if (j + 2 < nt) tile_addr(id + (j + 2) * G, nxt);
