@@ -753,10 +753,10 @@ void gemm256_kernel(KParams p) {
 #pragma unroll
   for (int i = 0; i < SUB; ++i) { read_a(fa0[i], 0, 0, i); read_b(fb0[i], 0, 0, i); }
 
-  // One stage = 2 k-steps x 4 groups of 4 MFMAs.  Group x of a step first
-  // issues one DMA instruction of the stage NBUF - 1 ahead (spread out so
-  // the vector memory queue never stalls the wave), then reads two fragments
-  // of the next k-step (B fragments first), then runs its 4 MFMAs.
+  // One stage = 2 k-steps x 4 groups of 4 MFMAs.  Group x of a step issues
+  // one DMA instruction of the stage NBUF - 1 ahead (spread out so the vector
+  // memory queue never stalls the wave) and reads two fragments of the next
+  // k-step (B fragments first), interleaved with its 4 MFMAs.
   int g = 0;                                  // global stage
   int bcur = 0;                               // its LDS buffer, g mod NBUF
   int epi_st = 0;                             // stores of the previous tile's epilogue (per lane)
@@ -783,31 +783,44 @@ void gemm256_kernel(KParams p) {
     static_for<2 * SUB>([&](auto gxc) {
       constexpr int gx = decltype(gxc)::value;
       constexpr int st = gx / SUB, x = gx % SUB;     // k-step, MFMA row block
+      // the group's instructions one by one between its MFMAs (each MFMA
+      // holds the matrix pipe for 32 cycles, hiding the issue of what
+      // follows it): MFMA, fragment read, MFMA, fragment read, MFMA, DMA,
+      // MFMA (measured on MI355X: 3-6 % faster than DMA and reads ahead of
+      // the four MFMAs)
       __builtin_amdgcn_sched_barrier(0);
-      if (iss) dma(ira, irb, ls, ib, gx);
-      // next k-step: step 1 of this stage, or step 0 of the next stage
-      if (!(LAST && st == 1)) {
-        const int ns = st == 0 ? bcur : bnext;
-        const int nst = st == 0 ? 1 : 0;
-        uint4 (&na)[SUB] = st == 0 ? fa1 : fa0;
-        uint4 (&nb)[SUB] = st == 0 ? fb1 : fb0;
-        if (x < 2) {
-          read_b(nb[2 * x], ns, nst, 2 * x);
-          read_b(nb[2 * x + 1], ns, nst, 2 * x + 1);
-        } else {
-          read_a(na[2 * x - 4], ns, nst, 2 * x - 4);
-          read_a(na[2 * x - 3], ns, nst, 2 * x - 3);
-        }
-      }
+      // fragments of the next k-step: step 1 of this stage, or step 0 of the next stage
+      const bool rd = !(LAST && st == 1);
+      const int ns = st == 0 ? bcur : bnext;
+      const int nst = st == 0 ? 1 : 0;
+      uint4 (&na)[SUB] = st == 0 ? fa1 : fa0;
+      uint4 (&nb)[SUB] = st == 0 ? fb1 : fb0;
       uint4 (&ca)[SUB] = st == 0 ? fa0 : fa1;
       uint4 (&cbv)[SUB] = st == 0 ? fb0 : fb1;
-#pragma unroll
-      for (int jj = 0; jj < SUB; ++jj) {
+      auto next_frag = [&](int h) {
+        if (!rd) return;
+        if (x < 2) read_b(nb[2 * x + h], ns, nst, 2 * x + h);
+        else read_a(na[2 * x - 4 + h], ns, nst, 2 * x - 4 + h);
+      };
+      auto mfma = [&](int jj) {
         const uint4& l = SWAP ? cbv[jj] : ca[x];
         const uint4& r = SWAP ? ca[x] : cbv[jj];
         if (FIRST && st == 0) Mma<T>::first(acc[x][jj], l, r);
         else Mma<T>::run(acc[x][jj], l, r);
-      }
+      };
+      mfma(0);
+      __builtin_amdgcn_sched_barrier(0);
+      next_frag(0);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma(1);
+      __builtin_amdgcn_sched_barrier(0);
+      next_frag(1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma(2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (iss) dma(ira, irb, ls, ib, gx);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma(3);
     });
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (ISS == 1) {
