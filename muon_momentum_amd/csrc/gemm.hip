@@ -416,6 +416,22 @@ __device__ __forceinline__ float acc_read(float v) {
   return r;
 }
 
+// Row chunks of a 32 x 32 block for 64-byte stores.  On entry lane L holds
+// the 16-byte chunks w0 (columns 8 (L/32) .. + 7) and w1 (columns 16 + 8 (L/32)
+// .. + 7) of block row L mod 32.  v_permlane16_swap exchanges the odd 16-lane
+// rows of its first operand with the even 16-lane rows of its second, which
+// leaves a = the chunk of block row L mod 16 and b = that of row 16 + L mod 16,
+// both at column 16 ((L / 16) mod 2) + 8 (L / 32): one store of a (or of b)
+// across the wave writes 16 rows x 64 contiguous bytes.
+__device__ __forceinline__ void rows64(const uint4& w0, const uint4& w1, uint4& a, uint4& b) {
+  const auto x = __builtin_amdgcn_permlane16_swap(w0.x, w1.x, false, false);
+  const auto y = __builtin_amdgcn_permlane16_swap(w0.y, w1.y, false, false);
+  const auto z = __builtin_amdgcn_permlane16_swap(w0.z, w1.z, false, false);
+  const auto w = __builtin_amdgcn_permlane16_swap(w0.w, w1.w, false, false);
+  a = make_uint4(x[0], y[0], z[0], w[0]);
+  b = make_uint4(x[1], y[1], z[1], w[1]);
+}
+
 struct TileAddr {
   int4v ra, rb;      // buffer resources based at the tile's first A row / B row or column
   int m0, n0, bat, ti, tj;
@@ -562,13 +578,14 @@ void gemm256_kernel(KParams p) {
       TO* C = (TO*)p.C + a.bat * p.sC;
       const int lc = lane & 31, lh = lane >> 5;
       TO* rowp = C + (long long)(a.m0 + wm * WT + lc) * p.ldc + (a.n0 + wn * WT);
+      // 16-bit output: rows lc mod 16 and 16 + lc mod 16, column chunk 16 ((lc / 16) mod 2) + 8 lh
+      TO* rowq = C + (long long)(a.m0 + wm * WT + (lc & 15)) * p.ldc + (a.n0 + wn * WT) + 16 * ((lc >> 4) & 1) + 8 * lh;
       static_for<SUB>([&](auto ic) {
         static_for<SUB>([&](auto jc) {
           constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
           // one block at a time: keeps the scheduler from moving every
           // accumulator into vector registers at once
           __builtin_amdgcn_sched_barrier(0);
-          TO* dst = rowp + (long long)(32 * i) * p.ldc + 32 * j;
           if constexpr (sizeof(TO) == 2) {
             uint32_t d[4][2];
             static_for<4>([&](auto gc) {
@@ -581,13 +598,20 @@ void gemm256_kernel(KParams p) {
                           ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
               });
             });
+            uint4 w[2];
             static_for<2>([&](auto pc) {
               constexpr int pr = decltype(pc)::value;
               const auto s0 = __builtin_amdgcn_permlane32_swap(d[2 * pr][0], d[2 * pr + 1][0], false, false);
               const auto s1 = __builtin_amdgcn_permlane32_swap(d[2 * pr][1], d[2 * pr + 1][1], false, false);
-              *(uint4*)(dst + 16 * pr + 8 * lh) = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+              w[pr] = make_uint4(s0[0], s1[0], s0[1], s1[1]);
             });
+            uint4 ra, rb;
+            rows64(w[0], w[1], ra, rb);
+            TO* q = rowq + (long long)(32 * i) * p.ldc + 32 * j;
+            *(uint4*)q = ra;
+            *(uint4*)(q + 16 * p.ldc) = rb;
           } else {
+            TO* dst = rowp + (long long)(32 * i) * p.ldc + 32 * j;
             static_for<4>([&](auto gc) {
               constexpr int g = decltype(gc)::value;
               *(float4*)(dst + 8 * g + 4 * lh) =
@@ -671,23 +695,31 @@ void gemm256_kernel(KParams p) {
                              ((uint32_t)__builtin_bit_cast(uint16_t, epi_round<TO>(v1)) << 16);
             });
           });
-          // direct: lane L < 32 columns 16 pr .. + 7, lane L + 32 columns 16 pr + 8 .. + 15
-          TO* drow = C + (rb0 + 32 * i + lc) * p.ldc + cb0 + 32 * j;
+          // direct: after the half-wave swap lane L holds columns 16 pr + 8 (L/32)
+          // .. + 7 of row L mod 32 (pr = 0, 1); rows64 regroups them into
+          // 64-byte row chunks of rows L mod 16 and 16 + L mod 16
+          uint4 wpr[2];
           static_for<2>([&](auto pc) {
             constexpr int pr = decltype(pc)::value;
             const auto s0 = __builtin_amdgcn_permlane32_swap(d[4 * pr], d[4 * pr + 2], false, false);
             const auto s1 = __builtin_amdgcn_permlane32_swap(d[4 * pr + 1], d[4 * pr + 3], false, false);
-            const uint4 w = make_uint4(s0[0], s1[0], s0[1], s1[1]);
-            const int y0 = 16 * pr + 8 * lh;
-            TO* dst = drow + y0;
-            if (!dblk || y0 + 7 <= lc) {
-              *(uint4*)dst = w;
-            } else if (y0 <= lc) {
+            wpr[pr] = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+          });
+          uint4 wr[2];
+          rows64(wpr[0], wpr[1], wr[0], wr[1]);
+          const int y0 = 16 * ((lc >> 4) & 1) + 8 * lh;       // block column of the chunk
+          static_for<2>([&](auto hc) {
+            constexpr int hh = decltype(hc)::value;
+            const int r = 16 * hh + (lc & 15);                 // block row of the chunk
+            TO* dst = C + (rb0 + 32 * i + r) * p.ldc + cb0 + 32 * j + y0;
+            if (!dblk || y0 + 7 <= r) {
+              *(uint4*)dst = wr[hh];
+            } else if (y0 <= r) {
               union { uint4 v; TO e[8]; } u;
-              u.v = w;
+              u.v = wr[hh];
 #pragma unroll
               for (int e = 0; e < 8; ++e)
-                if (y0 + e <= lc) dst[e] = u.e[e];
+                if (y0 + e <= r) dst[e] = u.e[e];
             }
           });
           // mirror: transpose the 8 dwords across the 8 lanes of the group

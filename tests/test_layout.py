@@ -123,19 +123,28 @@ def _symmetric_epilogue_writes(n):
                             if dq and i < j:
                                 continue
                             dblk = dq and i == j
-                            # direct: lane L < 32 columns 16 pr .. +7, lane L + 32 columns 16 pr + 8 .. +15
+                            # direct: after the half-wave swap lane L holds columns
+                            # 16 pr + 8 (L/32) .. +7 of row L mod 32 (w[pr][L]); the
+                            # 16-lane swap (rows64) then gives lane L the chunks of
+                            # rows L mod 16 and 16 + L mod 16 at column 16 ((L/16) mod 2) + 8 (L/32)
+                            w = [[[_acc(m0, n0, wm, wn, i, j, 32 * (((16 * pr + 8 * (L >> 5) + e) % 8) // 4) + (L & 31),
+                                        (16 * pr + 8 * (L >> 5) + e) // 8, (16 * pr + 8 * (L >> 5) + e) % 4)
+                                   for e in range(8)] for L in range(64)] for pr in range(2)]
                             for lane in range(64):
                                 lc, lh = lane & 31, lane >> 5
-                                for pr in range(2):
-                                    y0 = 16 * pr + 8 * lh
+                                odd = (lane >> 4) & 1
+                                a = w[1][lane - 16] if odd else w[0][lane]
+                                b = w[1][lane] if odd else w[0][lane + 16]
+                                y0 = 16 * ((lc >> 4) & 1) + 8 * lh
+                                for hh, chunk in ((0, a), (1, b)):
+                                    r = 16 * hh + (lc & 15)
                                     for e in range(8):
-                                        y = y0 + e
-                                        src = _acc(m0, n0, wm, wn, i, j, 32 * ((y % 8) // 4) + lc, y // 8, y % 4)
-                                        if dblk and y > lc:
+                                        if dblk and y0 + e > r:
                                             continue
-                                        pos = (m0 + wm * 128 + 32 * i + lc, n0 + wn * 128 + 32 * j + y)
+                                        pos = (m0 + wm * 128 + 32 * i + r, n0 + wn * 128 + 32 * j + y0 + e)
+                                        assert chunk[e] == pos       # a direct store holds its own entry
                                         assert pos not in written
-                                        written[pos] = src
+                                        written[pos] = chunk[e]
                             # mirror
                             d = [[(_acc(m0, n0, wm, wn, i, j, L, k >> 1, 2 * (k & 1)),
                                    _acc(m0, n0, wm, wn, i, j, L, k >> 1, 2 * (k & 1) + 1)) for k in range(8)]
