@@ -884,7 +884,9 @@ void gemm256_kernel(KParams p) {
   using IssNo = std::integral_constant<int, 0>;
   using IssTest = std::integral_constant<int, 2>;
   for (int j = 0; j < nt; ++j) {
-    stage(T1{}, T0{}, IssTest{}, j, 0);
+    // a tile's first stage has its look-ahead whenever a tile spans NBUF stages
+    if (KT >= NBUF) stage(T1{}, T0{}, IssYes{}, j, 0);
+    else stage(T1{}, T0{}, IssTest{}, j, 0);
     // stages whose look-ahead exists: all of a tile followed by another
     // (KT >= NBUF then), else those before the last NBUF - 1
     const int kt_iss = j + 1 < nt ? KT : KT - (NBUF - 1);
