@@ -406,6 +406,16 @@ __device__ __forceinline__ void wait_vm(int n) {
 #undef DION3_VM_CASE8
 #undef DION3_VM_CASE
 
+// End-of-stage barrier of the large-tile kernel.  The stage's DMA has been
+// waited for (vmcnt) before it; LDS reads need no wait here: every read of the
+// buffer the next DMA overwrites was consumed by an MFMA of this stage, and
+// the reads still in flight target the next stage's buffer.  (__syncthreads
+// would add a wait for all LDS reads, including those prefetched fragments.)
+// The memory clobber keeps the compiler from moving memory accesses across.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("s_barrier" ::: "memory");
+}
+
 typedef short short4v __attribute__((ext_vector_type(4)));
 
 // Read one accumulator out of its AGPR where it is used (an inline read keeps
@@ -864,7 +874,7 @@ void gemm256_kernel(KParams p) {
       } else {
         wait_vm(8 * (NBUF - 3));
       }
-      __syncthreads();
+      stage_barrier();
     } else if (g + 1 < GT) {
       // stage g + 2 must land before this barrier; later stages may fly on,
       // and so may the previous tile's epilogue stores when they were issued
@@ -873,7 +883,7 @@ void gemm256_kernel(KParams p) {
       int allowed = g + 2 < GT ? 8 * (last_issued - (g + 2)) : 0;
       if (MULTI && g + 2 < GT && j > 0 && kt < 2) allowed += epi_st;
       wait_vm(allowed < 63 ? allowed : 63);
-      __syncthreads();
+      stage_barrier();
     }
     ++g;
     bcur = bnext;
