@@ -588,38 +588,70 @@ void gemm256_kernel(KParams p) {
       TO* C = (TO*)p.C + a.bat * p.sC;
       const int lc = lane & 31, lh = lane >> 5;
       TO* rowp = C + (long long)(a.m0 + wm * WT + lc) * p.ldc + (a.n0 + wn * WT);
-      // 16-bit output: rows lc mod 16 and 16 + lc mod 16, column chunk 16 ((lc / 16) mod 2) + 8 lh
-      TO* rowq = C + (long long)(a.m0 + wm * WT + (lc & 15)) * p.ldc + (a.n0 + wn * WT) + 16 * ((lc >> 4) & 1) + 8 * lh;
+      // 16-bit output, blocks (i, 2 jp) and (i, 2 jp + 1) together: after
+      // rows64 lane L holds, for both blocks, the chunk at column
+      // 16 ((L / 16) mod 2) + 8 (L / 32) of block row r = L mod 16 (+ 16); lanes
+      // L and L ^ 8 (rows r and r ^ 8) exchange one chunk each (DPP rotation by
+      // 8 within 16 lanes), so that one store writes 8 rows x 128 contiguous
+      // bytes (64 columns)
+      const int hi8 = (lc >> 3) & 1;
+      TO* rowo = C + (long long)(a.m0 + wm * WT + (lc & 7)) * p.ldc + (a.n0 + wn * WT) + 32 * hi8 +
+                 16 * ((lc >> 4) & 1) + 8 * lh;
+      auto sel4 = [](bool c, const uint4 u, const uint4 v) {
+        return make_uint4(c ? u.x : v.x, c ? u.y : v.y, c ? u.z : v.z, c ? u.w : v.w);
+      };
+      auto xchg8 = [](const uint4& v) {
+        return make_uint4((unsigned)__builtin_amdgcn_mov_dpp((int)v.x, 0x128, 0xf, 0xf, false),
+                          (unsigned)__builtin_amdgcn_mov_dpp((int)v.y, 0x128, 0xf, 0xf, false),
+                          (unsigned)__builtin_amdgcn_mov_dpp((int)v.z, 0x128, 0xf, 0xf, false),
+                          (unsigned)__builtin_amdgcn_mov_dpp((int)v.w, 0x128, 0xf, 0xf, false));
+      };
+      // one block's results as two 64-byte row chunks per lane (rows64)
+      auto chunks = [&](auto ic, auto jc, uint4& ra, uint4& rb) {
+        if constexpr (sizeof(TO) == 2) {
+        constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
+        uint32_t d[4][2];
+        static_for<4>([&](auto gc) {
+          constexpr int g = decltype(gc)::value;
+          static_for<2>([&](auto hc) {
+            constexpr int h = decltype(hc)::value;
+            const TO lo = epi_round<TO>(p.alpha * acc_read(acc[i][j][4 * g + 2 * h]));
+            const TO hi = epi_round<TO>(p.alpha * acc_read(acc[i][j][4 * g + 2 * h + 1]));
+            d[g][h] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+          });
+        });
+        uint4 w[2];
+        static_for<2>([&](auto pc) {
+          constexpr int pr = decltype(pc)::value;
+          const auto s0 = __builtin_amdgcn_permlane32_swap(d[2 * pr][0], d[2 * pr + 1][0], false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(d[2 * pr][1], d[2 * pr + 1][1], false, false);
+          w[pr] = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+        });
+        rows64(w[0], w[1], ra, rb);
+        }
+      };
       static_for<SUB>([&](auto ic) {
         static_for<SUB>([&](auto jc) {
           constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
-          // one block at a time: keeps the scheduler from moving every
+          // one block (pair) at a time: keeps the scheduler from moving every
           // accumulator into vector registers at once
           __builtin_amdgcn_sched_barrier(0);
           if constexpr (sizeof(TO) == 2) {
-            uint32_t d[4][2];
-            static_for<4>([&](auto gc) {
-              constexpr int g = decltype(gc)::value;
+            if constexpr (j % 2 == 0) {
+              uint4 ra0, rb0, ra1, rb1;
+              chunks(ic, jc, ra0, rb0);
+              chunks(ic, std::integral_constant<int, j + 1>{}, ra1, rb1);
               static_for<2>([&](auto hc) {
-                constexpr int h = decltype(hc)::value;
-                const TO lo = epi_round<TO>(p.alpha * acc_read(acc[i][j][4 * g + 2 * h]));
-                const TO hi = epi_round<TO>(p.alpha * acc_read(acc[i][j][4 * g + 2 * h + 1]));
-                d[g][h] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-                          ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+                constexpr int hh = decltype(hc)::value;      // block rows 0-15 or 16-31
+                const uint4 x0 = hh ? rb0 : ra0;              // block j, row r (+ 16)
+                const uint4 x1 = hh ? rb1 : ra1;              // block j + 1, row r (+ 16)
+                const uint4 recv = xchg8(sel4(hi8, x0, x1));
+                TO* q = rowo + (long long)(32 * i + 16 * hh) * p.ldc + 32 * j;
+                *(uint4*)q = sel4(hi8, recv, x0);                 // row r mod 8 (+ 16)
+                *(uint4*)(q + 8 * p.ldc) = sel4(hi8, x1, recv);   // row 8 + r mod 8 (+ 16)
               });
-            });
-            uint4 w[2];
-            static_for<2>([&](auto pc) {
-              constexpr int pr = decltype(pc)::value;
-              const auto s0 = __builtin_amdgcn_permlane32_swap(d[2 * pr][0], d[2 * pr + 1][0], false, false);
-              const auto s1 = __builtin_amdgcn_permlane32_swap(d[2 * pr][1], d[2 * pr + 1][1], false, false);
-              w[pr] = make_uint4(s0[0], s1[0], s0[1], s1[1]);
-            });
-            uint4 ra, rb;
-            rows64(w[0], w[1], ra, rb);
-            TO* q = rowq + (long long)(32 * i) * p.ldc + 32 * j;
-            *(uint4*)q = ra;
-            *(uint4*)(q + 16 * p.ldc) = rb;
+            }
           } else {
             TO* dst = rowp + (long long)(32 * i) * p.ldc + 32 * j;
             static_for<4>([&](auto gc) {

@@ -171,3 +171,51 @@ def test_symmetric_epilogue_writes_every_entry_once_from_the_lower_triangle():
         for (x, y), (r, c) in w.items():
             assert r >= c                      # computed at or below the diagonal
             assert (x, y) in ((r, c), (c, r))  # stored at its place or the mirrored one
+
+
+# ---------------------------------------------------------------------------
+# Q X epilogue of the 256 x 256 kernel (gemm.hip: epilogue_swap, 16-bit
+# output): half-wave swap, 16-lane swap (rows64) and the exchange between
+# lanes L and L ^ 8 (DPP rotation by 8 within 16 lanes), then 8 rows x 128
+# bytes per store.  Every entry of the tile is written once, with its own value.
+
+
+def _qx_chunks(wm, wn, i, j):
+    """rows64 output per lane: (ra, rb), each 8 (row, column) entries of the tile."""
+    w = [[[_acc(0, 0, wm, wn, i, j, 32 * (((16 * pr + 8 * (L >> 5) + e) % 8) // 4) + (L & 31),
+                (16 * pr + 8 * (L >> 5) + e) // 8, (16 * pr + 8 * (L >> 5) + e) % 4)
+           for e in range(8)] for L in range(64)] for pr in range(2)]
+    ra, rb = [], []
+    for L in range(64):
+        odd = (L >> 4) & 1
+        ra.append(w[1][L - 16] if odd else w[0][L])
+        rb.append(w[1][L] if odd else w[0][L + 16])
+    return ra, rb
+
+
+def test_qx_epilogue_writes_every_entry_once():
+    written = {}
+    for wm in range(2):
+        for wn in range(2):
+            for i in range(4):
+                for j in (0, 2):
+                    ra0, rb0 = _qx_chunks(wm, wn, i, j)
+                    ra1, rb1 = _qx_chunks(wm, wn, i, j + 1)
+                    for hh in range(2):
+                        x0 = rb0 if hh else ra0
+                        x1 = rb1 if hh else ra1
+                        send = [x0[L] if (L >> 3) & 1 else x1[L] for L in range(64)]
+                        recv = [send[(L & ~15) | ((L + 8) & 15)] for L in range(64)]   # row_ror:8
+                        for L in range(64):
+                            lc, lh = L & 31, L >> 5
+                            hi8 = (lc >> 3) & 1
+                            col = 32 * j + 32 * hi8 + 16 * ((lc >> 4) & 1) + 8 * lh
+                            for rowoff, chunk in ((0, recv[L] if hi8 else x0[L]), (8, x1[L] if hi8 else recv[L])):
+                                row = wm * 128 + 32 * i + 16 * hh + (lc & 7) + rowoff
+                                for e in range(8):
+                                    pos = (row, wn * 128 + col + e)
+                                    assert chunk[e] == pos
+                                    assert pos not in written
+                                    written[pos] = True
+    assert len(written) == 256 * 256
+    # one store: 8 rows x 64 columns (128 contiguous bytes per row)
