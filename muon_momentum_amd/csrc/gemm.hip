@@ -442,6 +442,18 @@ __device__ __forceinline__ void rows64(const uint4& w0, const uint4& w1, uint4& 
   b = make_uint4(x[1], y[1], z[1], w[1]);
 }
 
+__device__ __forceinline__ uint4 sel4(bool c, const uint4 u, const uint4 v) {
+  return make_uint4(c ? u.x : v.x, c ? u.y : v.y, c ? u.z : v.z, c ? u.w : v.w);
+}
+
+// Exchange between lanes L and L ^ 8 (DPP row rotation by 8 within 16 lanes).
+__device__ __forceinline__ uint4 xchg8(const uint4& v) {
+  return make_uint4((unsigned)__builtin_amdgcn_mov_dpp((int)v.x, 0x128, 0xf, 0xf, false),
+                    (unsigned)__builtin_amdgcn_mov_dpp((int)v.y, 0x128, 0xf, 0xf, false),
+                    (unsigned)__builtin_amdgcn_mov_dpp((int)v.z, 0x128, 0xf, 0xf, false),
+                    (unsigned)__builtin_amdgcn_mov_dpp((int)v.w, 0x128, 0xf, 0xf, false));
+}
+
 struct TileAddr {
   int4v ra, rb;      // buffer resources based at the tile's first A row / B row or column
   int m0, n0, bat, ti, tj;
@@ -597,15 +609,6 @@ void gemm256_kernel(KParams p) {
       const int hi8 = (lc >> 3) & 1;
       TO* rowo = C + (long long)(a.m0 + wm * WT + (lc & 7)) * p.ldc + (a.n0 + wn * WT) + 32 * hi8 +
                  16 * ((lc >> 4) & 1) + 8 * lh;
-      auto sel4 = [](bool c, const uint4 u, const uint4 v) {
-        return make_uint4(c ? u.x : v.x, c ? u.y : v.y, c ? u.z : v.z, c ? u.w : v.w);
-      };
-      auto xchg8 = [](const uint4& v) {
-        return make_uint4((unsigned)__builtin_amdgcn_mov_dpp((int)v.x, 0x128, 0xf, 0xf, false),
-                          (unsigned)__builtin_amdgcn_mov_dpp((int)v.y, 0x128, 0xf, 0xf, false),
-                          (unsigned)__builtin_amdgcn_mov_dpp((int)v.z, 0x128, 0xf, 0xf, false),
-                          (unsigned)__builtin_amdgcn_mov_dpp((int)v.w, 0x128, 0xf, 0xf, false));
-      };
       // one block's results as two 64-byte row chunks per lane (rows64)
       auto chunks = [&](auto ic, auto jc, uint4& ra, uint4& rb) {
         if constexpr (sizeof(TO) == 2) {
@@ -710,45 +713,126 @@ void gemm256_kernel(KParams p) {
         });
         wait_vm(0);
       }
+      // packed results of block (i, j): dword 2 g + h holds columns 8 g + 4 (lane/32) + 2 h, + 1
+      auto pack = [&](auto ic, auto jc, bool dblk, uint32_t (&d)[8]) {
+        constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
+        static_for<4>([&](auto gc) {
+          constexpr int g = decltype(gc)::value;
+          static_for<2>([&](auto hc) {
+            constexpr int h = decltype(hc)::value;
+            float v0 = p.alpha * acc_read(acc[i][j][4 * g + 2 * h]);
+            float v1 = p.alpha * acc_read(acc[i][j][4 * g + 2 * h + 1]);
+            if (use_e) {
+              const uint32_t ew = h ? epk[i][j][g].y : epk[i][j][g].x;
+              v0 = __builtin_fmaf(p.beta, Store<TO>::to_f32(__builtin_bit_cast(TO, (uint16_t)(ew & 0xffffu))), v0);
+              v1 = __builtin_fmaf(p.beta, Store<TO>::to_f32(__builtin_bit_cast(TO, (uint16_t)(ew >> 16))), v1);
+            }
+            if (OP == OP_SQ_ADD && dblk) {
+              if (8 * g + 4 * lh + 2 * h == lc) v0 += p.gamma;
+              if (8 * g + 4 * lh + 2 * h + 1 == lc) v1 += p.gamma;
+            }
+            d[2 * g + h] = (uint32_t)__builtin_bit_cast(uint16_t, epi_round<TO>(v0)) |
+                           ((uint32_t)__builtin_bit_cast(uint16_t, epi_round<TO>(v1)) << 16);
+          });
+        });
+      };
+      // after the half-wave swap lane L holds columns 16 pr + 8 (L/32) .. + 7 of
+      // row L mod 32 (pr = 0, 1); rows64 regroups them into 64-byte row chunks
+      // of rows L mod 16 (wr[0]) and 16 + L mod 16 (wr[1])
+      auto direct_chunks = [&](const uint32_t (&d)[8], uint4 (&wr)[2]) {
+        uint4 wpr[2];
+        static_for<2>([&](auto pc) {
+          constexpr int pr = decltype(pc)::value;
+          const auto s0 = __builtin_amdgcn_permlane32_swap(d[4 * pr], d[4 * pr + 2], false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(d[4 * pr + 1], d[4 * pr + 3], false, false);
+          wpr[pr] = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+        });
+        rows64(wpr[0], wpr[1], wr[0], wr[1]);
+      };
+      // mirror: transpose the 8 dwords across the 8 lanes of the group, then
+      // 16-byte chunks of rows c0 and c0 + 1 of the transposed position
+      auto mirror = [&](auto ic, auto jc, bool dblk, uint32_t (&d)[8]) {
+        constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
+        static_for<3>([&](auto sc) {
+          constexpr int s = 4 >> decltype(sc)::value;
+          const bool up = (t & s) != 0;
+          static_for<8>([&](auto kc) {
+            constexpr int k = decltype(kc)::value;
+            if constexpr ((k & s) == 0) {
+              constexpr int kk = k | s;
+              const uint32_t send = up ? d[k] : d[kk];
+              const uint32_t recv =
+                  (uint32_t)__builtin_amdgcn_ds_swizzle((int)send, (s << 10) | 0x1f);
+              if (up) d[k] = recv;
+              else d[kk] = recv;
+            }
+          });
+        });
+        // dword k now holds row 8 o + k, columns c0 (low half) and c0 + 1
+        const uint4 ma = make_uint4((d[0] & 0xffffu) | (d[1] << 16), (d[2] & 0xffffu) | (d[3] << 16),
+                                    (d[4] & 0xffffu) | (d[5] << 16), (d[6] & 0xffffu) | (d[7] << 16));
+        const uint4 mb = make_uint4((d[0] >> 16) | (d[1] & 0xffff0000u), (d[2] >> 16) | (d[3] & 0xffff0000u),
+                                    (d[4] >> 16) | (d[5] & 0xffff0000u), (d[6] >> 16) | (d[7] & 0xffff0000u));
+        const int c0 = 8 * (t >> 1) + 4 * lh + 2 * (t & 1);
+        TO* mrow = C + (cb0 + 32 * j + c0) * p.ldc + rb0 + 32 * i + 8 * o;
+        static_for<2>([&](auto bc) {
+          constexpr int b = decltype(bc)::value;
+          const uint4& w = b ? mb : ma;
+          const int y = c0 + b;                 // block column = transposed row
+          TO* dst = mrow + b * p.ldc;
+          if (!dblk || 8 * o > y) {
+            *(uint4*)dst = w;
+          } else if (8 * o + 7 > y) {
+            union { uint4 v; TO e[8]; } u;
+            u.v = w;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (8 * o + e > y) dst[e] = u.e[e];
+          }
+        });
+      };
+      // (the symmetric product only: with the A^2 + B and X X^T epilogues the
+      // pairing raised register use and slowed their main loop)
+      if (OP == OP_SYM_MUL && !dq) {
+        // a full quadrant: blocks (i, j) and (i, j + 1) stored together, lanes L
+        // and L ^ 8 exchanging one chunk each (DPP rotation by 8 within 16
+        // lanes), so that a direct store writes 8 rows x 128 contiguous bytes
+        const int hi8 = (lc >> 3) & 1;
+        TO* rowo = C + (rb0 + (lc & 7)) * p.ldc + cb0 + 32 * hi8 + 16 * ((lc >> 4) & 1) + 8 * lh;
+        static_for<SUB>([&](auto ic) {
+          static_for<SUB / 2>([&](auto jpc) {
+            constexpr int i = decltype(ic)::value, j = 2 * decltype(jpc)::value;
+            __builtin_amdgcn_sched_barrier(0);
+            uint32_t d0[8], d1[8];
+            pack(ic, std::integral_constant<int, j>{}, false, d0);
+            pack(ic, std::integral_constant<int, j + 1>{}, false, d1);
+            uint4 w0[2], w1[2];
+            direct_chunks(d0, w0);
+            direct_chunks(d1, w1);
+            static_for<2>([&](auto hc) {
+              constexpr int hh = decltype(hc)::value;       // block rows 0-15 or 16-31
+              const uint4 recv = xchg8(sel4(hi8, w0[hh], w1[hh]));
+              TO* q = rowo + (32 * i + 16 * hh) * p.ldc + 32 * j;
+              *(uint4*)q = sel4(hi8, recv, w0[hh]);                 // row r mod 8 (+ 16)
+              *(uint4*)(q + 8 * p.ldc) = sel4(hi8, w1[hh], recv);   // row 8 + r mod 8 (+ 16)
+            });
+            mirror(ic, std::integral_constant<int, j>{}, false, d0);
+            mirror(ic, std::integral_constant<int, j + 1>{}, false, d1);
+            nst += 8;
+          });
+        });
+        return nst;
+      }
       static_for<SUB>([&](auto ic) {
         static_for<SUB>([&](auto jc) {
           constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
-          if (dq && i < j) return;
+          if (dq && i < j) return;              // above the diagonal of a diagonal quadrant
           const bool dblk = dq && i == j;
           __builtin_amdgcn_sched_barrier(0);
-          // packed results: dword 2 g + h holds columns 8 g + 4 (lane/32) + 2 h, + 1
           uint32_t d[8];
-          static_for<4>([&](auto gc) {
-            constexpr int g = decltype(gc)::value;
-            static_for<2>([&](auto hc) {
-              constexpr int h = decltype(hc)::value;
-              float v0 = p.alpha * acc_read(acc[i][j][4 * g + 2 * h]);
-              float v1 = p.alpha * acc_read(acc[i][j][4 * g + 2 * h + 1]);
-              if (use_e) {
-                const uint32_t ew = h ? epk[i][j][g].y : epk[i][j][g].x;
-                v0 = __builtin_fmaf(p.beta, Store<TO>::to_f32(__builtin_bit_cast(TO, (uint16_t)(ew & 0xffffu))), v0);
-                v1 = __builtin_fmaf(p.beta, Store<TO>::to_f32(__builtin_bit_cast(TO, (uint16_t)(ew >> 16))), v1);
-              }
-              if (OP == OP_SQ_ADD && dblk) {
-                if (8 * g + 4 * lh + 2 * h == lc) v0 += p.gamma;
-                if (8 * g + 4 * lh + 2 * h + 1 == lc) v1 += p.gamma;
-              }
-              d[2 * g + h] = (uint32_t)__builtin_bit_cast(uint16_t, epi_round<TO>(v0)) |
-                             ((uint32_t)__builtin_bit_cast(uint16_t, epi_round<TO>(v1)) << 16);
-            });
-          });
-          // direct: after the half-wave swap lane L holds columns 16 pr + 8 (L/32)
-          // .. + 7 of row L mod 32 (pr = 0, 1); rows64 regroups them into
-          // 64-byte row chunks of rows L mod 16 and 16 + L mod 16
-          uint4 wpr[2];
-          static_for<2>([&](auto pc) {
-            constexpr int pr = decltype(pc)::value;
-            const auto s0 = __builtin_amdgcn_permlane32_swap(d[4 * pr], d[4 * pr + 2], false, false);
-            const auto s1 = __builtin_amdgcn_permlane32_swap(d[4 * pr + 1], d[4 * pr + 3], false, false);
-            wpr[pr] = make_uint4(s0[0], s1[0], s0[1], s1[1]);
-          });
+          pack(ic, jc, dblk, d);
           uint4 wr[2];
-          rows64(wpr[0], wpr[1], wr[0], wr[1]);
+          direct_chunks(d, wr);
           const int y0 = 16 * ((lc >> 4) & 1) + 8 * lh;       // block column of the chunk
           static_for<2>([&](auto hc) {
             constexpr int hh = decltype(hc)::value;
@@ -764,44 +848,7 @@ void gemm256_kernel(KParams p) {
                 if (y0 + e <= r) dst[e] = u.e[e];
             }
           });
-          // mirror: transpose the 8 dwords across the 8 lanes of the group
-          static_for<3>([&](auto sc) {
-            constexpr int s = 4 >> decltype(sc)::value;
-            const bool up = (t & s) != 0;
-            static_for<8>([&](auto kc) {
-              constexpr int k = decltype(kc)::value;
-              if constexpr ((k & s) == 0) {
-                constexpr int kk = k | s;
-                const uint32_t send = up ? d[k] : d[kk];
-                const uint32_t recv =
-                    (uint32_t)__builtin_amdgcn_ds_swizzle((int)send, (s << 10) | 0x1f);
-                if (up) d[k] = recv;
-                else d[kk] = recv;
-              }
-            });
-          });
-          // dword k now holds row 8 o + k, columns c0 (low half) and c0 + 1
-          const uint4 ma = make_uint4((d[0] & 0xffffu) | (d[1] << 16), (d[2] & 0xffffu) | (d[3] << 16),
-                                      (d[4] & 0xffffu) | (d[5] << 16), (d[6] & 0xffffu) | (d[7] << 16));
-          const uint4 mb = make_uint4((d[0] >> 16) | (d[1] & 0xffff0000u), (d[2] >> 16) | (d[3] & 0xffff0000u),
-                                      (d[4] >> 16) | (d[5] & 0xffff0000u), (d[6] >> 16) | (d[7] & 0xffff0000u));
-          const int c0 = 8 * (t >> 1) + 4 * lh + 2 * (t & 1);
-          TO* mrow = C + (cb0 + 32 * j + c0) * p.ldc + rb0 + 32 * i + 8 * o;
-          static_for<2>([&](auto bc) {
-            constexpr int b = decltype(bc)::value;
-            const uint4& w = b ? mb : ma;
-            const int y = c0 + b;                 // block column = transposed row
-            TO* dst = mrow + b * p.ldc;
-            if (!dblk || 8 * o > y) {
-              *(uint4*)dst = w;
-            } else if (8 * o + 7 > y) {
-              union { uint4 v; TO e[8]; } u;
-              u.v = w;
-#pragma unroll
-              for (int e = 0; e < 8; ++e)
-                if (8 * o + e > y) dst[e] = u.e[e];
-            }
-          });
+          mirror(ic, jc, dblk, d);
           if (!dblk) nst += 4;
         });
       });

@@ -107,7 +107,7 @@ def _butterfly(X):
     return X
 
 
-def _symmetric_epilogue_writes(n):
+def _symmetric_epilogue_writes(n, paired):
     written = {}
     T = n // 256
     for ti in range(T):
@@ -118,6 +118,31 @@ def _symmetric_epilogue_writes(n):
                     if diag and wm < wn:
                         continue
                     dq = diag and wm == wn
+                    if paired and not dq:
+                        # a full quadrant of the symmetric product: direct stores of
+                        # blocks (i, j), (i, j + 1) together (lanes L and L ^ 8
+                        # exchange one chunk each)
+                        for i in range(4):
+                            for j in (0, 2):
+                                ra0, rb0 = _qx_chunks(wm, wn, i, j)
+                                ra1, rb1 = _qx_chunks(wm, wn, i, j + 1)
+                                for hh in range(2):
+                                    x0 = rb0 if hh else ra0
+                                    x1 = rb1 if hh else ra1
+                                    send = [x0[L] if (L >> 3) & 1 else x1[L] for L in range(64)]
+                                    recv = [send[(L & ~15) | ((L + 8) & 15)] for L in range(64)]
+                                    for L in range(64):
+                                        lc, lh = L & 31, L >> 5
+                                        hi8 = (lc >> 3) & 1
+                                        col = n0 + wn * 128 + 32 * j + 32 * hi8 + 16 * ((lc >> 4) & 1) + 8 * lh
+                                        for rowoff, chunk in ((0, recv[L] if hi8 else x0[L]), (8, x1[L] if hi8 else recv[L])):
+                                            row = m0 + wm * 128 + 32 * i + 16 * hh + (lc & 7) + rowoff
+                                            for e in range(8):
+                                                pos = (row, col + e)
+                                                src = (chunk[e][0] + m0, chunk[e][1] + n0)
+                                                assert src == pos
+                                                assert pos not in written
+                                                written[pos] = src
                     for i in range(4):
                         for j in range(4):
                             if dq and i < j:
@@ -130,7 +155,7 @@ def _symmetric_epilogue_writes(n):
                             w = [[[_acc(m0, n0, wm, wn, i, j, 32 * (((16 * pr + 8 * (L >> 5) + e) % 8) // 4) + (L & 31),
                                         (16 * pr + 8 * (L >> 5) + e) // 8, (16 * pr + 8 * (L >> 5) + e) % 4)
                                    for e in range(8)] for L in range(64)] for pr in range(2)]
-                            for lane in range(64):
+                            for lane in range(64 if dq or not paired else 0):
                                 lc, lh = lane & 31, lane >> 5
                                 odd = (lane >> 4) & 1
                                 a = w[1][lane - 16] if odd else w[0][lane]
@@ -165,8 +190,8 @@ def _symmetric_epilogue_writes(n):
 
 
 def test_symmetric_epilogue_writes_every_entry_once_from_the_lower_triangle():
-    for n in (256, 768):
-        w = _symmetric_epilogue_writes(n)
+    for n, paired in ((256, False), (768, False), (768, True)):
+        w = _symmetric_epilogue_writes(n, paired)
         assert len(w) == n * n
         for (x, y), (r, c) in w.items():
             assert r >= c                      # computed at or below the diagonal
