@@ -749,10 +749,11 @@ void gemm256_kernel(KParams p) {
         });
         rows64(wpr[0], wpr[1], wr[0], wr[1]);
       };
-      // mirror: transpose the 8 dwords across the 8 lanes of the group, then
-      // 16-byte chunks of rows c0 and c0 + 1 of the transposed position
-      auto mirror = [&](auto ic, auto jc, bool dblk, uint32_t (&d)[8]) {
-        constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
+      // mirror: transpose the 8 dwords across the 8 lanes of the group (lane t
+      // = lane mod 8 of group o = (lane mod 32) / 8), which leaves 16-byte
+      // chunks of rows c0 (ma) and c0 + 1 (mb) of the transposed position,
+      // c0 = 8 (t/2) + 4 (lane/32) + 2 (t mod 2), columns 8 o .. + 7 of the block
+      auto mirror_chunks = [&](uint32_t (&d)[8], uint4& ma, uint4& mb) {
         static_for<3>([&](auto sc) {
           constexpr int s = 4 >> decltype(sc)::value;
           const bool up = (t & s) != 0;
@@ -769,11 +770,16 @@ void gemm256_kernel(KParams p) {
           });
         });
         // dword k now holds row 8 o + k, columns c0 (low half) and c0 + 1
-        const uint4 ma = make_uint4((d[0] & 0xffffu) | (d[1] << 16), (d[2] & 0xffffu) | (d[3] << 16),
-                                    (d[4] & 0xffffu) | (d[5] << 16), (d[6] & 0xffffu) | (d[7] << 16));
-        const uint4 mb = make_uint4((d[0] >> 16) | (d[1] & 0xffff0000u), (d[2] >> 16) | (d[3] & 0xffff0000u),
-                                    (d[4] >> 16) | (d[5] & 0xffff0000u), (d[6] >> 16) | (d[7] & 0xffff0000u));
-        const int c0 = 8 * (t >> 1) + 4 * lh + 2 * (t & 1);
+        ma = make_uint4((d[0] & 0xffffu) | (d[1] << 16), (d[2] & 0xffffu) | (d[3] << 16),
+                        (d[4] & 0xffffu) | (d[5] << 16), (d[6] & 0xffffu) | (d[7] << 16));
+        mb = make_uint4((d[0] >> 16) | (d[1] & 0xffff0000u), (d[2] >> 16) | (d[3] & 0xffff0000u),
+                        (d[4] >> 16) | (d[5] & 0xffff0000u), (d[6] >> 16) | (d[7] & 0xffff0000u));
+      };
+      const int c0 = 8 * (t >> 1) + 4 * lh + 2 * (t & 1);
+      auto mirror = [&](auto ic, auto jc, bool dblk, uint32_t (&d)[8]) {
+        constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
+        uint4 ma, mb;
+        mirror_chunks(d, ma, mb);
         TO* mrow = C + (cb0 + 32 * j + c0) * p.ldc + rb0 + 32 * i + 8 * o;
         static_for<2>([&](auto bc) {
           constexpr int b = decltype(bc)::value;
@@ -799,26 +805,60 @@ void gemm256_kernel(KParams p) {
         // lanes), so that a direct store writes 8 rows x 128 contiguous bytes
         const int hi8 = (lc >> 3) & 1;
         TO* rowo = C + (rb0 + (lc & 7)) * p.ldc + cb0 + 32 * hi8 + 16 * ((lc >> 4) & 1) + 8 * lh;
-        static_for<SUB>([&](auto ic) {
+        // mirror stores of blocks (i, j) and (i + 1, j) together: lanes t and
+        // t ^ 1 (rows c0 and c0 + 2 of the transposed position) exchange one
+        // chunk each (DPP quad permutation [1, 0, 3, 2]), so that one store
+        // writes 8 transposed rows x 128 contiguous bytes
+        const int t1 = t & 1;
+        TO* mrow2 = C + (cb0 + c0 - 2 * t1) * p.ldc + rb0 + 32 * t1 + 8 * o;
+        auto swap1 = [](const uint4& v) {
+          return make_uint4((unsigned)__builtin_amdgcn_mov_dpp((int)v.x, 0xB1, 0xf, 0xf, false),
+                            (unsigned)__builtin_amdgcn_mov_dpp((int)v.y, 0xB1, 0xf, 0xf, false),
+                            (unsigned)__builtin_amdgcn_mov_dpp((int)v.z, 0xB1, 0xf, 0xf, false),
+                            (unsigned)__builtin_amdgcn_mov_dpp((int)v.w, 0xB1, 0xf, 0xf, false));
+        };
+        static_for<SUB / 2>([&](auto ipc) {
           static_for<SUB / 2>([&](auto jpc) {
-            constexpr int i = decltype(ic)::value, j = 2 * decltype(jpc)::value;
+            constexpr int i = 2 * decltype(ipc)::value, j = 2 * decltype(jpc)::value;
             __builtin_amdgcn_sched_barrier(0);
-            uint32_t d0[8], d1[8];
-            pack(ic, std::integral_constant<int, j>{}, false, d0);
-            pack(ic, std::integral_constant<int, j + 1>{}, false, d1);
-            uint4 w0[2], w1[2];
-            direct_chunks(d0, w0);
-            direct_chunks(d1, w1);
-            static_for<2>([&](auto hc) {
-              constexpr int hh = decltype(hc)::value;       // block rows 0-15 or 16-31
-              const uint4 recv = xchg8(sel4(hi8, w0[hh], w1[hh]));
-              TO* q = rowo + (32 * i + 16 * hh) * p.ldc + 32 * j;
-              *(uint4*)q = sel4(hi8, recv, w0[hh]);                 // row r mod 8 (+ 16)
-              *(uint4*)(q + 8 * p.ldc) = sel4(hi8, w1[hh], recv);   // row 8 + r mod 8 (+ 16)
+            uint32_t d[2][2][8];                       // blocks (i + a, j + b)
+            static_for<2>([&](auto ac) {
+              static_for<2>([&](auto bc) {
+                constexpr int a2 = decltype(ac)::value, b2 = decltype(bc)::value;
+                pack(std::integral_constant<int, i + a2>{}, std::integral_constant<int, j + b2>{}, false, d[a2][b2]);
+              });
             });
-            mirror(ic, std::integral_constant<int, j>{}, false, d0);
-            mirror(ic, std::integral_constant<int, j + 1>{}, false, d1);
-            nst += 8;
+            // direct: blocks (i + a, j) and (i + a, j + 1)
+            static_for<2>([&](auto ac) {
+              constexpr int a2 = decltype(ac)::value;
+              uint4 w0[2], w1[2];
+              direct_chunks(d[a2][0], w0);
+              direct_chunks(d[a2][1], w1);
+              static_for<2>([&](auto hc) {
+                constexpr int hh = decltype(hc)::value;       // block rows 0-15 or 16-31
+                const uint4 recv = xchg8(sel4(hi8, w0[hh], w1[hh]));
+                TO* q = rowo + (32 * (i + a2) + 16 * hh) * p.ldc + 32 * j;
+                *(uint4*)q = sel4(hi8, recv, w0[hh]);                 // row r mod 8 (+ 16)
+                *(uint4*)(q + 8 * p.ldc) = sel4(hi8, w1[hh], recv);   // row 8 + r mod 8 (+ 16)
+              });
+            });
+            // mirror: blocks (i, j + b) and (i + 1, j + b)
+            static_for<2>([&](auto bc) {
+              constexpr int b2 = decltype(bc)::value;
+              uint4 m0a, m0b, m1a, m1b;                  // block rows i and i + 1
+              mirror_chunks(d[0][b2], m0a, m0b);
+              mirror_chunks(d[1][b2], m1a, m1b);
+              static_for<2>([&](auto rc) {
+                constexpr int rr = decltype(rc)::value;      // transposed row c0 + rr
+                const uint4& x0 = rr ? m0b : m0a;
+                const uint4& x1 = rr ? m1b : m1a;
+                const uint4 recv = swap1(sel4(t1, x0, x1));
+                TO* q = mrow2 + (32 * (j + b2) + rr) * p.ldc + 32 * i;
+                *(uint4*)q = sel4(t1, recv, x0);                      // row c0 - 2 t1 + rr
+                *(uint4*)(q + 2 * p.ldc) = sel4(t1, x1, recv);        // row c0 - 2 t1 + 2 + rr
+              });
+            });
+            nst += 16;
           });
         });
         return nst;

@@ -107,6 +107,15 @@ def _butterfly(X):
     return X
 
 
+def _mirror_chunks(m0, n0, wm, wn, i, j):
+    """Butterfly output of block (i, j): Y[lane][e][b] is the entry of block row
+    8 o + e and column c0 + b that lane holds for the mirrored store."""
+    d = [[(_acc(m0, n0, wm, wn, i, j, L, k >> 1, 2 * (k & 1)),
+           _acc(m0, n0, wm, wn, i, j, L, k >> 1, 2 * (k & 1) + 1)) for k in range(8)]
+         for L in range(64)]
+    return _butterfly(d)
+
+
 def _symmetric_epilogue_writes(n, paired):
     written = {}
     T = n // 256
@@ -143,6 +152,30 @@ def _symmetric_epilogue_writes(n, paired):
                                                 assert src == pos
                                                 assert pos not in written
                                                 written[pos] = src
+                        # mirror stores of blocks (i, j) and (i + 1, j) together (lanes
+                        # t and t ^ 1 exchange one chunk each)
+                        for i in (0, 2):
+                            for j in range(4):
+                                Y0 = _mirror_chunks(m0, n0, wm, wn, i, j)
+                                Y1 = _mirror_chunks(m0, n0, wm, wn, i + 1, j)
+                                for rr in range(2):
+                                    x0 = [[Y0[L][e][rr] for e in range(8)] for L in range(64)]
+                                    x1 = [[Y1[L][e][rr] for e in range(8)] for L in range(64)]
+                                    send = [x0[L] if L & 1 else x1[L] for L in range(64)]
+                                    recv = [send[L ^ 1] for L in range(64)]
+                                    for L in range(64):
+                                        lc, lh = L & 31, L >> 5
+                                        o, t = lc >> 3, lc & 7
+                                        t1 = t & 1
+                                        c0 = 8 * (t >> 1) + 4 * lh + 2 * t1
+                                        col = m0 + wm * 128 + 32 * (i + t1) + 8 * o
+                                        for rowoff, chunk in ((0, recv[L] if t1 else x0[L]), (2, x1[L] if t1 else recv[L])):
+                                            row = n0 + wn * 128 + 32 * j + c0 - 2 * t1 + rr + rowoff
+                                            for e in range(8):
+                                                pos = (row, col + e)
+                                                assert chunk[e] == (pos[1], pos[0])   # the mirrored entry
+                                                assert pos not in written
+                                                written[pos] = chunk[e]
                     for i in range(4):
                         for j in range(4):
                             if dq and i < j:
@@ -171,11 +204,8 @@ def _symmetric_epilogue_writes(n, paired):
                                         assert pos not in written
                                         written[pos] = chunk[e]
                             # mirror
-                            d = [[(_acc(m0, n0, wm, wn, i, j, L, k >> 1, 2 * (k & 1)),
-                                   _acc(m0, n0, wm, wn, i, j, L, k >> 1, 2 * (k & 1) + 1)) for k in range(8)]
-                                 for L in range(64)]
-                            Y = _butterfly(d)
-                            for lane in range(64):
+                            Y = _mirror_chunks(m0, n0, wm, wn, i, j)
+                            for lane in range(64 if dq or not paired else 0):
                                 lc, lh = lane & 31, lane >> 5
                                 o, t = lc >> 3, lc & 7
                                 c0 = 8 * (t >> 1) + 4 * lh + 2 * (t & 1)
