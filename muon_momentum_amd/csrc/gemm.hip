@@ -1126,8 +1126,15 @@ static int launch_typed(const GemmArgs& a, hipStream_t s) {
   static const char* names[4] = {"syrk", "sym_sq_add", "sym_mul", "gemm_qx"};
   TimedLaunch tl(names[OP], s);
   if (big) {
-    if constexpr (HALF)
-      hipLaunchKernelGGL((gemm256_kernel<T, TO, OP, kStages>), dim3((unsigned)wgs), dim3(kThreads), 0, s, p);
+    // X X^T without the beta C term is the symmetric product kernel with
+    // B = A (same schedule, main loop and epilogue arithmetic; the epilogue
+    // operand of beta != 0 costs registers)
+    if constexpr (HALF) {
+      if (OP == OP_SYRK && a.E == nullptr)
+        hipLaunchKernelGGL((gemm256_kernel<T, TO, OP_SYM_MUL, kStages>), dim3((unsigned)wgs), dim3(kThreads), 0, s, p);
+      else
+        hipLaunchKernelGGL((gemm256_kernel<T, TO, OP, kStages>), dim3((unsigned)wgs), dim3(kThreads), 0, s, p);
+    }
   } else if (fast_for(BM))
     hipLaunchKernelGGL((gemm_kernel<T, TO, OP, false, BM>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
   else
