@@ -1130,9 +1130,12 @@ static int launch_typed(const GemmArgs& a, hipStream_t s) {
     // B = A (same schedule, main loop and epilogue arithmetic; the epilogue
     // operand of beta != 0 costs registers)
     if constexpr (HALF) {
-      if (OP == OP_SYRK && a.E == nullptr)
-        hipLaunchKernelGGL((gemm256_kernel<T, TO, OP_SYM_MUL, kStages>), dim3((unsigned)wgs), dim3(kThreads), 0, s, p);
-      else
+      bool sym_mul_kernel = false;
+      if constexpr (OP == OP_SYRK) sym_mul_kernel = a.E == nullptr;
+      if constexpr (OP == OP_SYRK)
+        if (sym_mul_kernel)
+          hipLaunchKernelGGL((gemm256_kernel<T, TO, OP_SYM_MUL, kStages>), dim3((unsigned)wgs), dim3(kThreads), 0, s, p);
+      if (!sym_mul_kernel)
         hipLaunchKernelGGL((gemm256_kernel<T, TO, OP, kStages>), dim3((unsigned)wgs), dim3(kThreads), 0, s, p);
     }
   } else if (fast_for(BM))
