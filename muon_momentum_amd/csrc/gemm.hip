@@ -698,23 +698,29 @@ void gemm256_kernel(KParams p) {
       const int o = lc >> 3, t = lc & 7;
       const long long rb0 = a.m0 + wm * WT;       // first C row of the quadrant
       const long long cb0 = a.n0 + wn * WT;       // first C column of the quadrant
-      uint2 epk[SUB][SUB][4];
-      if (use_e) {
+      // the epilogue operand: X X^T with beta != 0 loads all of it up front;
+      // A^2 + B loads it per block group, one group ahead (fewer registers)
+      constexpr bool EGROUP = OP == OP_SQ_ADD;
+      uint2 epk[EGROUP ? 1 : SUB][EGROUP ? 1 : SUB][4];
+      if (!EGROUP && use_e) {
         static_for<SUB>([&](auto ic) {
           static_for<SUB>([&](auto jc) {
             constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
             if (dq && i < j) return;
-            const TO* er = E + (rb0 + 32 * i + lc) * p.lde + cb0 + 32 * j + 4 * lh;
-            static_for<4>([&](auto gc) {
-              constexpr int g = decltype(gc)::value;
-              epk[i][j][g] = *(const uint2*)(er + 8 * g);
-            });
+            if constexpr (!EGROUP) {
+              const TO* er = E + (rb0 + 32 * i + lc) * p.lde + cb0 + 32 * j + 4 * lh;
+              static_for<4>([&](auto gc) {
+                constexpr int g = decltype(gc)::value;
+                epk[i][j][g] = *(const uint2*)(er + 8 * g);
+              });
+            }
           });
         });
         wait_vm(0);
       }
       // packed results of block (i, j): dword 2 g + h holds columns 8 g + 4 (lane/32) + 2 h, + 1
-      auto pack = [&](auto ic, auto jc, bool dblk, uint32_t (&d)[8]) {
+      // ev: the block's epilogue operand words (read only when use_e)
+      auto pack = [&](auto ic, auto jc, bool dblk, uint32_t (&d)[8], const uint2 (&ev)[4]) {
         constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
         static_for<4>([&](auto gc) {
           constexpr int g = decltype(gc)::value;
@@ -723,7 +729,7 @@ void gemm256_kernel(KParams p) {
             float v0 = p.alpha * acc_read(acc[i][j][4 * g + 2 * h]);
             float v1 = p.alpha * acc_read(acc[i][j][4 * g + 2 * h + 1]);
             if (use_e) {
-              const uint32_t ew = h ? epk[i][j][g].y : epk[i][j][g].x;
+              const uint32_t ew = h ? ev[g].y : ev[g].x;
               v0 = __builtin_fmaf(p.beta, Store<TO>::to_f32(__builtin_bit_cast(TO, (uint16_t)(ew & 0xffffu))), v0);
               v1 = __builtin_fmaf(p.beta, Store<TO>::to_f32(__builtin_bit_cast(TO, (uint16_t)(ew >> 16))), v1);
             }
@@ -735,6 +741,11 @@ void gemm256_kernel(KParams p) {
                            ((uint32_t)__builtin_bit_cast(uint16_t, epi_round<TO>(v1)) << 16);
           });
         });
+      };
+      auto load_e = [&](int i, int j, uint2 (&ev)[4]) {
+        const TO* er = E + (rb0 + 32 * i + lc) * p.lde + cb0 + 32 * j + 4 * lh;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) ev[g] = *(const uint2*)(er + 8 * g);
       };
       // after the half-wave swap lane L holds columns 16 pr + 8 (L/32) .. + 7 of
       // row L mod 32 (pr = 0, 1); rows64 regroups them into 64-byte row chunks
@@ -799,7 +810,7 @@ void gemm256_kernel(KParams p) {
       };
       // (the symmetric product only: with the A^2 + B and X X^T epilogues the
       // pairing raised register use and slowed their main loop)
-      if (OP == OP_SYM_MUL && !dq) {
+      if ((OP == OP_SYM_MUL || OP == OP_SQ_ADD) && !dq) {
         // a full quadrant: blocks (i, j) and (i, j + 1) stored together, lanes L
         // and L ^ 8 exchanging one chunk each (DPP rotation by 8 within 16
         // lanes), so that a direct store writes 8 rows x 128 contiguous bytes
@@ -817,15 +828,28 @@ void gemm256_kernel(KParams p) {
                             (unsigned)__builtin_amdgcn_mov_dpp((int)v.z, 0xB1, 0xf, 0xf, false),
                             (unsigned)__builtin_amdgcn_mov_dpp((int)v.w, 0xB1, 0xf, 0xf, false));
         };
+        // A^2 + B: the epilogue operand of group q is loaded during group q - 1
+        uint2 eg[2][2][2][4];
+        auto load_group = [&](int i, int j, uint2 (&e)[2][2][4]) {
+          load_e(i, j, e[0][0]); load_e(i, j + 1, e[0][1]);
+          load_e(i + 1, j, e[1][0]); load_e(i + 1, j + 1, e[1][1]);
+        };
+        if (OP == OP_SQ_ADD) load_group(0, 0, eg[0]);
         static_for<SUB / 2>([&](auto ipc) {
           static_for<SUB / 2>([&](auto jpc) {
             constexpr int i = 2 * decltype(ipc)::value, j = 2 * decltype(jpc)::value;
+            constexpr int q = (i / 2) * (SUB / 2) + j / 2, qb = q & 1;
             __builtin_amdgcn_sched_barrier(0);
+            if constexpr (OP == OP_SQ_ADD && q + 1 < (SUB / 2) * (SUB / 2)) {
+              constexpr int qn = q + 1;
+              load_group(2 * (qn / (SUB / 2)), 2 * (qn % (SUB / 2)), eg[qb ^ 1]);
+            }
             uint32_t d[2][2][8];                       // blocks (i + a, j + b)
             static_for<2>([&](auto ac) {
               static_for<2>([&](auto bc) {
                 constexpr int a2 = decltype(ac)::value, b2 = decltype(bc)::value;
-                pack(std::integral_constant<int, i + a2>{}, std::integral_constant<int, j + b2>{}, false, d[a2][b2]);
+                pack(std::integral_constant<int, i + a2>{}, std::integral_constant<int, j + b2>{}, false, d[a2][b2],
+                     eg[qb][a2][b2]);
               });
             });
             // direct: blocks (i + a, j) and (i + a, j + 1)
@@ -863,14 +887,24 @@ void gemm256_kernel(KParams p) {
         });
         return nst;
       }
+      // A^2 + B on a diagonal quadrant: blocks (i, j <= i) in order, the
+      // epilogue operand of the next one loaded during this one
+      uint2 eb[2][4];
+      if (EGROUP) load_e(0, 0, eb[0]);
       static_for<SUB>([&](auto ic) {
         static_for<SUB>([&](auto jc) {
           constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
           if (dq && i < j) return;              // above the diagonal of a diagonal quadrant
           const bool dblk = dq && i == j;
           __builtin_amdgcn_sched_barrier(0);
+          constexpr int bq = i * (i + 1) / 2 + j, bb = bq & 1;   // position among blocks j <= i
+          if constexpr (EGROUP) {
+            if constexpr (j < i) load_e(i, j + 1, eb[bb ^ 1]);
+            else if constexpr (i + 1 < SUB) load_e(i + 1, 0, eb[bb ^ 1]);
+          }
           uint32_t d[8];
-          pack(ic, jc, dblk, d);
+          if constexpr (EGROUP) pack(ic, jc, dblk, d, eb[bb]);
+          else pack(ic, jc, dblk, d, epk[EGROUP ? 0 : i][EGROUP ? 0 : j]);
           uint4 wr[2];
           direct_chunks(d, wr);
           const int y0 = 16 * ((lc >> 4) & 1) + 8 * lh;       // block column of the chunk
