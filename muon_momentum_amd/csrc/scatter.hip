@@ -24,13 +24,22 @@ template <> struct Pack8<float> { union U { uint4 v[2]; float e[8]; }; };
 
 template <typename T>
 __device__ __forceinline__ void load8(typename Pack8<T>::U& u, const T* p) {
+  // every byte these passes touch is touched once: non-temporal accesses
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
 #pragma unroll
-  for (int w = 0; w < (int)(8 * sizeof(T) / 16); ++w) u.v[w] = ((const uint4*)p)[w];
+  for (int w = 0; w < (int)(8 * sizeof(T) / 16); ++w) {
+    const v4u x = __builtin_nontemporal_load((const v4u*)p + w);
+    u.v[w] = make_uint4(x.x, x.y, x.z, x.w);
+  }
 }
 template <typename T>
 __device__ __forceinline__ void store8(T* p, const typename Pack8<T>::U& u) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
 #pragma unroll
-  for (int w = 0; w < (int)(8 * sizeof(T) / 16); ++w) ((uint4*)p)[w] = u.v[w];
+  for (int w = 0; w < (int)(8 * sizeof(T) / 16); ++w) {
+    const v4u x = {u.v[w].x, u.v[w].y, u.v[w].z, u.v[w].w};
+    __builtin_nontemporal_store(x, (v4u*)p + w);
+  }
 }
 
 // w' = round(fp32(a - eta o)) with a = fp32(u w) when decaying, else w.
