@@ -319,10 +319,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(KParams p) {
 // Q X runs several tiles per work-group: the stage sequence continues from one
 // tile into the next, so the next tile's first stages are loaded while the
 // current tile finishes, and the MFMA computes C^T blocks (operands swapped),
-// which leaves four consecutive columns of one row in each lane; one lane swap
-// across the two half-waves then forms 16-byte row chunks, and a tile is
-// written with 32 stores per wave that stay in flight while the next tile
-// computes.
+// which leaves four consecutive columns of one row in each lane; lane swaps
+// across the half-waves and 16-lane rows form 16-byte row chunks, and an
+// exchange between lanes L and L ^ 8 of two neighbouring blocks lets each
+// store write 8 rows x 128 contiguous bytes; a tile is written with 32 stores
+// per lane that stay in flight while the next tile computes.
 // ---------------------------------------------------------------------------
 template <int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -673,8 +674,10 @@ void gemm256_kernel(KParams p) {
 
   // Symmetric epilogue (several tiles per work-group, no LDS).  Block (i, j)
   // of the wave holds C[r][c] for r = lane%32 and c = 8 g + 4 (lane/32) + q in
-  // acc[i][j][4 g + q] (the Q X layout).  Direct part: the Q X stores, 16-byte
-  // chunks of row r.  Mirror part: in each group of 8 lanes (rows 8 o .. 8 o + 7
+  // acc[i][j][4 g + q] (the Q X layout).  Direct part: 16-byte chunks of rows
+  // r mod 16 and 16 + r mod 16 (rows64); on full quadrants of the symmetric
+  // product and A^2 + B, blocks (i, j) and (i, j + 1) are stored together as in
+  // Q X (8 rows x 128 bytes per store).  Mirror part: in each group of 8 lanes (rows 8 o .. 8 o + 7
   // of the block), a butterfly transpose of the 8 packed dwords over lane
   // distances 4, 2, 1 leaves lane t = lane%8 the 8 rows of columns
   // c0 = 8 (t/2) + 4 (lane/32) + 2 (t mod 2) and c0 + 1, which are 16-byte
@@ -683,9 +686,13 @@ void gemm256_kernel(KParams p) {
   // the one below), blocks above the diagonal of the two diagonal quadrants
   // likewise, and on a diagonal block the direct chunk keeps columns <= row
   // and the mirror chunk rows > column, so every entry is written once, from
-  // the value computed at or below the diagonal.  The epilogue operand is read
-  // at the direct position and waited for before any store.  Returns the
-  // number of stores every lane issues (a lower bound of the wave's count).
+  // the value computed at or below the diagonal; on full quadrants of those two
+  // kernels the mirror chunks of blocks (i, j) and (i + 1, j) are stored
+  // together after lanes t and t ^ 1 exchange one chunk (8 transposed rows x
+  // 128 bytes per store).  The epilogue operand is read at the direct
+  // position: by X X^T with beta all up front, by A^2 + B per block group one
+  // group ahead.  Returns the number of stores every lane issues (a lower
+  // bound of the wave's count).
   auto epilogue_sym = [&](const TileAddr& a) -> int {
     int nst = 0;
     if constexpr (SYM) {
