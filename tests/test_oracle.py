@@ -378,6 +378,61 @@ def test_fp16_storage_model_within_tolerance():
     assert rel(O.ns_gram_rounded(X, store="f32"), ref) < 1e-5
 
 
+# The fp16 storage model, replayed in exact rational arithmetic: every product
+# and every polynomial is formed exactly and each stored intermediate (the
+# normalised input, R, Z, Q, Z R, Z R Z and the pass output) is rounded once to
+# the storage format.  `skip` names one intermediate left unrounded and `fmt`
+# may name the wrong format: the planted mistakes of the storage model.
+STORED = ("x0", "R", "Z", "Q", "ZR", "ZRZ", "X")
+
+
+def _rounded_gram_exact(X, coeffs, restart_after, fmt="f16", skip=None):
+    n, m = X.shape
+    rnd = lambda A, what: A if what == skip else [[Fraction(_exact_round(v, fmt)) for v in row] for row in A]
+    mm = lambda A, B: [[sum((A[i][t] * B[t][j] for t in range(len(B))), Fraction(0)) for j in range(len(B[0]))]
+                       for i in range(len(A))]
+    tr = lambda A: [list(col) for col in zip(*A)]
+    # the normalisation divides by the same fp64 norm the oracle computes
+    nrm = Fraction(math.sqrt(float(np.sum(X * X))) + O.DEFAULT_EPS)
+    Xf = rnd([[Fraction(float(v)) / nrm for v in row] for row in X], "x0")
+    for t0, t1 in O.dion3._passes(len(coeffs), restart_after):
+        R = rnd(mm(Xf, tr(Xf)), "R")
+        Q = None
+        for t in range(t0, t1):
+            a, b, c = (Fraction(v) for v in coeffs[t])
+            R2 = mm(R, R)
+            Z = rnd([[(a if i == j else 0) + b * R[i][j] + c * R2[i][j] for j in range(n)] for i in range(n)], "Z")
+            Q = Z if Q is None else rnd(mm(Q, Z), "Q")
+            if t < t1 - 1:
+                R = rnd(mm(rnd(mm(Z, R), "ZR"), Z), "ZRZ")
+        Xf = rnd(mm(Q, Xf), "X")
+    return np.array([[float(v) for v in row] for row in Xf])
+
+
+def test_fp16_storage_model_is_exact_rounding():
+    """ns_gram_rounded rounds every stored intermediate once, to fp16 (the
+    pages switch the Gram iteration to float16, paper §4): on a 2 x 3 input with
+    T = 3 and a restart after iteration 2 (so the Z R Z update, the Q Z
+    product and the restart all occur), it equals the exact-rational replay bit
+    for bit, and replays that skip any one rounding, or round to bf16 or not at
+    all, differ from it."""
+    X = np.array([[1.375, 0.5, 0.0], [-0.875, -0.75, -1.75]])
+    coeffs, restart = O.DEFAULT_COEFFS[:3], (2,)
+    want = _rounded_gram_exact(X, coeffs, restart)
+    got = O.ns_gram_rounded(X, coeffs, restart, store="f16")
+    assert np.array_equal(got, want)
+    assert np.array_equal(O.round_to(got, "f16"), got)          # outputs are fp16 values
+    # the planted mistakes of the storage model are each visible in the output
+    for what in STORED:
+        assert not np.array_equal(_rounded_gram_exact(X, coeffs, restart, skip=what), want), what
+    assert not np.array_equal(_rounded_gram_exact(X, coeffs, restart, fmt="bf16"), want)
+    assert not np.array_equal(O.ns_gram_rounded(X, coeffs, restart, store="bf16"), want)
+    assert not np.array_equal(O.ns_gram_rounded(X, coeffs, restart, store="f64"), want)
+    # and with fp32 storage the oracle matches the fp32 replay
+    assert np.array_equal(O.ns_gram_rounded(X, coeffs, restart, store="f32"),
+                          _rounded_gram_exact(X, coeffs, restart, fmt="f32"))
+
+
 # ------------------------------------------------------ planted mistakes fail
 def _gram_variant(X, mistake, coeffs=O.DEFAULT_COEFFS, restart_after=(2,)):
     X = O.frobenius_normalize(X)
