@@ -10,10 +10,11 @@ applied by the next step's momentum pass (deferred, bit-identical).  Inputs are 
 resident in HBM before the timed region starts; the momentum state carries
 across steps.
 
-Prints one JSON line: step milliseconds (the headline), the roofline of the
-kernel that takes the most time per step (algorithmic bytes or FLOPs per
-launch over its average launch duration, from HIP events recorded around every
-library launch during the timed steps), a per-kernel table, the symmetric-GEMM
+Prints one JSON line: step milliseconds (the headline, timed with no
+per-launch instrumentation), the roofline of the kernel that takes the most
+time per step (algorithmic bytes or FLOPs per launch over its average launch
+duration, from HIP events recorded around every library launch during a
+separate instrumented pass of the same steps), a per-kernel table, the symmetric-GEMM
 microbenchmark (C = A A^T and C = A^2 + B on n x n fp16/bf16) and the CPU
 oracle timed on a bounded sample of the same workload.
 """
@@ -47,6 +48,8 @@ def parse():
     ap.add_argument("--f", type=float, default=0.25)
     ap.add_argument("--flavor", default="muon", choices=["muon", "normuon"],
                     help="update flavour (NorMuon: beta2 = 0.95, eps = 1e-8)")
+    ap.add_argument("--profile-steps", type=int, default=10,
+                    help="steps of the separate instrumented pass that gives the per-kernel table")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-microbench", action="store_true")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
@@ -123,10 +126,10 @@ def kernel_work(groups, ks, ns_bytes=2, store_bytes=2):
     return {name: (kind[name], v) for name, v in w.items()}
 
 
-def cpu_baseline(groups, ks, f, eta, set_name, budget_s=12.0, max_mats=12):
-    """The oracle's whole step on matrices of the first shape group (attention
-    projections) until about `budget_s` seconds have elapsed, scaled to the
-    full set by parameter count."""
+def cpu_baseline(groups, ks, f, eta, set_name, budget_s=16.0, max_per_group=6):
+    """The oracle's whole step on sampled matrices of every shape group (at
+    least one each, more while the group's share of `budget_s` lasts); each
+    group's time per matrix is scaled by that group's matrix count."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -134,27 +137,27 @@ def cpu_baseline(groups, ks, f, eta, set_name, budget_s=12.0, max_mats=12):
     from muon_momentum_amd import synth
 
     threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-    rows, cols, b = groups[0]
-    k = ks[0]
-    spent, done = 0.0, 0
-    while done < min(b, max_mats) and (done == 0 or spent < budget_s):
-        W = synth.weights(rows, cols, 1, dtype="bf16", group_seed=1000 + done)[0]
-        G = synth.gradient(rows, cols, 1, dtype="bf16", group_seed=1000 + done, step=0)[0]
-        Wh = W.float().numpy().astype(np.float64)
-        Gh = G.float().numpy().astype(np.float64)
-        Mh = np.zeros_like(Gh)
-        t0 = time.perf_counter()
-        O.dion3_step(Wh, Mh, Gh, k=k, mu=MU, eta=eta, fmt="bf16")
-        spent += time.perf_counter() - t0
-        done += 1
-    params_sample = done * rows * cols
-    params_total = sum(r * c * bb for r, c, bb in groups)
-    per_step_s = spent * params_total / params_sample
-    return {"value": round(per_step_s * 1e3, 1), "unit": "ms per step (extrapolated)",
+    total_s, spent_all, parts = 0.0, 0.0, []
+    for gi, ((rows, cols, b), k) in enumerate(zip(groups, ks)):
+        spent, done = 0.0, 0
+        while done < min(b, max_per_group) and (done == 0 or spent < budget_s / len(groups)):
+            W = synth.weights(rows, cols, 1, dtype="bf16", group_seed=1000 + 97 * gi + done)[0]
+            G = synth.gradient(rows, cols, 1, dtype="bf16", group_seed=1000 + 97 * gi + done, step=0)[0]
+            Wh = W.float().numpy().astype(np.float64)
+            Gh = G.float().numpy().astype(np.float64)
+            Mh = np.zeros_like(Gh)
+            t0 = time.perf_counter()
+            O.dion3_step(Wh, Mh, Gh, k=k, mu=MU, eta=eta, fmt="bf16")
+            spent += time.perf_counter() - t0
+            done += 1
+        total_s += spent / done * b
+        spent_all += spent
+        parts.append(f"{done} of {b} {rows}x{cols}")
+    return {"value": round(total_s * 1e3, 1), "unit": "ms per step (extrapolated)",
             "cores": int(threads), "kind": "oracle",
-            "sample": (f"fp64 NumPy oracle, whole step on {done} of the {b} {rows}x{cols} matrices of "
-                       f"the {set_name} set at f={f:g} ({spent:.1f} s measured), scaled to the set's "
-                       f"{params_total / 1e9:.2f} G parameters by parameter count")}
+            "sample": (f"fp64 NumPy oracle, whole step on {', '.join(parts)} matrices of the {set_name} set "
+                       f"at f={f:g} ({spent_all:.1f} s measured); each group's time per matrix scaled by its "
+                       f"matrix count")}
 
 
 # ------------------------------------------------------------- the GPU parts
@@ -201,10 +204,9 @@ def run_step_bench(d, synth, torch, args):
     torch.cuda.synchronize()
     host_ms = sorted(host)[len(host) // 2]
 
-    launches_per_step = 64
-    d.dion3_timing_enable(launches_per_step * args.steps + 64)
-    # one event between consecutive steps: the mean over the timed region and
-    # the per-step median / 90th percentile
+    # the headline: K steps with no per-launch instrumentation, one event
+    # between consecutive steps (the mean over the timed region and the
+    # per-step median / 90th percentile)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     ev[0].record()
@@ -216,16 +218,32 @@ def run_step_bench(d, synth, torch, args):
     per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     pct = {"p50": per_step[len(per_step) // 2],
            "p90": per_step[min(len(per_step) - 1, int(math.ceil(0.9 * len(per_step))) - 1)]}
+    print(f"# timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+
+    # a separate instrumented pass for the per-kernel table: a HIP event pair
+    # around every library launch, on the stream of the launch
+    nprof = max(1, min(args.steps, args.profile_steps))
+    launches_per_step = 96
+    d.dion3_timing_enable(launches_per_step * nprof + 64)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(nprof):
+        one_step(True)
+    e1.record()
+    torch.cuda.synchronize()
+    pct["instrumented"] = e0.elapsed_time(e1) / nprof
+    pct["profile_steps"] = nprof
     per_kernel = d.dion3_timing_report()
     d.dion3_timing_enable(0)
-    print(f"# timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+    print(f"# instrumented {nprof} steps: {pct['instrumented']:.3f} ms/step", file=sys.stderr, flush=True)
 
     work = kernel_work(groups, ks)
     table = {}
     for name, (cnt, total_ms) in per_kernel.items():
         kind, units = work.get(name, ("?", 0.0))
-        launches = cnt / args.steps
-        step_ms = total_ms / args.steps
+        launches = cnt / nprof
+        step_ms = total_ms / nprof
         avg_us = 1e3 * total_ms / cnt
         if kind == "hbm":
             ach = units / (step_ms * 1e-3) / 1e9
@@ -325,6 +343,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "ms_per_step_p50": round(pct["p50"], 3), "ms_per_step_p90": round(pct["p90"], 3),
         "host_ms_per_step": round(pct["host"], 3),
+        "ms_per_step_instrumented": round(pct["instrumented"], 3),
+        "profile_steps": pct["profile_steps"],
         "data": "synthetic (Gaussian gradients with log-normal line scales, seeded)",
         "config": {"workload": f"{args.set} shape set Dion3 step, f={args.f:g}"
                                + ("" if args.flavor == "muon" else ", NorMuon flavour"),

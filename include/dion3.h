@@ -131,24 +131,48 @@ int dion3_gather_rows(const dion3_group* g, const void* M, const int32_t* idx, i
 
 /* -------------------------------------------------- Gram Newton-Schulz */
 
-/* Workspace bytes dion3_gram_ns needs. */
-size_t dion3_gram_ns_workspace_bytes(int batch, int k, int m, int ns_dtype);
+/* Workspace bytes dion3_gram_ns needs for k selected lines of this group
+ * (0 if the arguments are invalid, e.g. k > m). */
+size_t dion3_gram_ns_workspace_bytes(const dion3_group* g, int k, const dion3_ns_params* p);
 
-/* Gram Newton-Schulz with restarts (Section 4) on already normalised inputs.
+/* One workspace size that serves both dion3_momentum_rowsel and dion3_gram_ns
+ * for this group and k (the larger of the two). */
+size_t dion3_workspace_bytes(const dion3_group* g, int k, const dion3_ns_params* p);
+
+/* Gram Newton-Schulz of every matrix's selected submatrix (Section 2: the
+ * input is normalised by its Frobenius norm; Section 4: Gram iteration with
+ * restarts).  Per matrix b, with S = idx[b] ([batch][k] ascending canonical
+ * lines, as produced by dion3_momentum_rowsel):
+ *   X0 = M[S,:] / (||M[S,:]||_F + p->eps)   (norm accumulated in fp64, fixed
+ *        order; X0 rounded once to p->ns_dtype), then dion3_gram_ns_gathered.
+ *   M   [batch][rows][cols] in g->dtype (DION3_F32 or DION3_BF16), read only.
+ *   O   out [batch][k][m] in p->ns_dtype, canonical orientation, packed.
+ * Requires k <= m.  ws holds the sums of squares, X0 and the iteration's
+ * buffers (dion3_gram_ns_workspace_bytes).  An index outside [0, n) is
+ * treated as an all-zero line. */
+int dion3_gram_ns(const dion3_group* g, const void* M, const int32_t* idx, int k,
+                  const dion3_ns_params* p, void* O, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes dion3_gram_ns_gathered needs. */
+size_t dion3_gram_ns_gathered_workspace_bytes(int batch, int k, int m, int ns_dtype);
+
+/* Gram Newton-Schulz with restarts (Section 4) on already gathered and
+ * normalised inputs (dion3_gather_rows); the whole-step driver uses this form.
  *   X0  [batch][k][m] in p->ns_dtype, k <= m, read only.
  *   O   out [batch][k][m] in p->ns_dtype: the Newton-Schulz output.
  * Per pass on R = X X^T:  Z = a I + b R + c R^2;  Q = Z (first iteration) or
  * Q Z;  R = Z R Z (except on the last iteration); the pass ends X <- Q X.
  * Symmetric products compute the lower triangle and mirror it. */
-int dion3_gram_ns(int batch, int k, int m, const dion3_ns_params* p, const void* X0,
-                  void* O, void* ws, size_t ws_bytes, void* stream);
+int dion3_gram_ns_gathered(int batch, int k, int m, const dion3_ns_params* p, const void* X0,
+                           void* O, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes dion3_standard_ns needs. */
 size_t dion3_standard_ns_workspace_bytes(int batch, int k, int m, int ns_dtype);
 
 /* Standard Newton-Schulz on the symmetric kernels (Section 2 for the
  * iteration; Section 4 and Appendix C.3: the fall-back used when the aspect
- * ratio m / k is 1).  Arguments as dion3_gram_ns; p->restart_mask is ignored.
+ * ratio m / k is 1).  Arguments as dion3_gram_ns_gathered; p->restart_mask is
+ * ignored.
  * Per iteration t: A = X X^T, Z = a_t I + b_t A + c_t A^2, X <- Z X, i.e.
  * X <- a_t X + (b_t A + c_t A^2) X with the a_t X term carried by Z. */
 int dion3_standard_ns(int batch, int k, int m, const dion3_ns_params* p, const void* X0,
@@ -289,6 +313,17 @@ int dion3_step_normuon(int n_groups, const dion3_group* groups, void* const* W, 
                        const void* const* G, const int* k, int32_t* const* idx, float* const* V,
                        int deferred, int has_prev, const dion3_ns_params* p, float eta, float wd,
                        float mu, float beta2, float nm_eps, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------- teardown */
+
+/* Destroys what the library created by itself: the whole-step streams and
+ * event pool of every device that ran a step, and the timing events.  Call it
+ * before the process's HIP runtime shuts down (the Python binding does, at
+ * interpreter exit); work already enqueued on the library streams completes
+ * first.  A later call of a whole-step entry point creates them again.  Not
+ * to be called while another thread runs a library call.  Returns DION3_OK or
+ * DION3_ERR_HIP. */
+int dion3_release(void);
 
 /* ------------------------------------------------------------ measurement */
 

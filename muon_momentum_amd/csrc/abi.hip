@@ -118,3 +118,13 @@ extern "C" int dion3_timing_report(char* buf, size_t buf_bytes) {
   }
   return (int)off;
 }
+
+// Releases everything the library created on its own: the whole-step streams
+// and event pool of every device and the timing events.  A later call creates
+// what it needs again.  Nothing is released that was never created, so a
+// process that never used the GPU makes no HIP call here.
+extern "C" int dion3_release(void) {
+  const int a = release_step_resources();
+  const int b = g_timing.cap > 0 || !g_timing.ev.empty() ? dion3_timing_enable(0) : DION3_OK;
+  return a ? a : b;
+}

@@ -126,6 +126,14 @@ inline bool canonical_dims(const dion3_group* g, int* n, int* m, int* axis) {
   return true;
 }
 
+// Destroys the streams and events the whole-step driver created (step.hip).
+int release_step_resources();
+
+// ||M[S,:]||_F^2 of every matrix of a group (scatter.hip); line_ws holds
+// [batch][k] fp64 per-line sums.
+int selected_sqnorm(const dion3_group* g, int axis, const void* M, const int32_t* idx, int k,
+                    double* line_ws, double* sqn, hipStream_t s);
+
 // ------------------------------------------------- GEMM launchers (gemm.hip)
 enum GemmOp { OP_SYRK = 0, OP_SQ_ADD = 1, OP_SYM_MUL = 2, OP_GEMM = 3 };
 

@@ -99,19 +99,19 @@ extern "C" int dion3_gemm(int batch, int k, int m, int in_dtype, const void* Q, 
                (hipStream_t)stream);
 }
 
-extern "C" size_t dion3_gram_ns_workspace_bytes(int batch, int k, int m, int ns_dtype) {
+extern "C" size_t dion3_gram_ns_gathered_workspace_bytes(int batch, int k, int m, int ns_dtype) {
   if (batch < 1 || k < 1 || m < 1 || !ns_dtype_ok(ns_dtype)) return 0;
   const size_t es = dtype_size(ns_dtype);
   return align256((size_t)batch * k * m * es) + 4 * align256((size_t)batch * k * k * es);
 }
 
-extern "C" int dion3_gram_ns(int batch, int k, int m, const dion3_ns_params* p, const void* X0,
-                             void* O, void* ws, size_t ws_bytes, void* stream) {
+extern "C" int dion3_gram_ns_gathered(int batch, int k, int m, const dion3_ns_params* p, const void* X0,
+                                      void* O, void* ws, size_t ws_bytes, void* stream) {
   if (batch < 1 || k < 1 || m < 1 || k > m || !p || !X0 || !O || X0 == O) return DION3_ERR_INVALID_ARG;
   if (p->T < 1 || !p->coeffs || !ns_dtype_ok(p->ns_dtype)) return DION3_ERR_INVALID_ARG;
   for (int i = 0; i < 3 * p->T; ++i)
     if (!(p->coeffs[i] == p->coeffs[i])) return DION3_ERR_INVALID_ARG;
-  const size_t need = dion3_gram_ns_workspace_bytes(batch, k, m, p->ns_dtype);
+  const size_t need = dion3_gram_ns_gathered_workspace_bytes(batch, k, m, p->ns_dtype);
   if (!ws || ws_bytes < need) return DION3_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   const int dt = p->ns_dtype;
@@ -182,6 +182,58 @@ extern "C" int dion3_gram_ns(int batch, int k, int m, const dion3_ns_params* p, 
     give(R);
     cur = out;
   }
+  return st;
+}
+
+// Gram Newton-Schulz of a group's selected submatrices, from M and the
+// selection ("Dion3: Full-Stack Orthogonal Updates", Section 2 for the
+// Frobenius normalisation of the input, Section 4 for the iteration).  The
+// workspace holds the per-line and per-matrix sums of squares, X0 and the
+// scratch of the gathered form.
+static size_t gram_group_parts(const dion3_group* g, int k, const dion3_ns_params* p, int* n, int* m,
+                               int* axis, size_t part[4]) {
+  if (!p || !canonical_dims(g, n, m, axis) || k < 1 || k > *n || k > *m || !ns_dtype_ok(p->ns_dtype)) return 0;
+  const size_t es = dtype_size(p->ns_dtype);
+  part[0] = align256((size_t)g->batch * k * sizeof(double));    // per-line sums of squares
+  part[1] = align256((size_t)g->batch * sizeof(double));        // ||M[S,:]||_F^2 per matrix
+  part[2] = align256((size_t)g->batch * k * *m * es);           // X0
+  part[3] = dion3_gram_ns_gathered_workspace_bytes(g->batch, k, *m, p->ns_dtype);
+  return part[3] ? part[0] + part[1] + part[2] + part[3] : 0;
+}
+
+extern "C" size_t dion3_gram_ns_workspace_bytes(const dion3_group* g, int k, const dion3_ns_params* p) {
+  int n, m, axis;
+  size_t part[4];
+  return gram_group_parts(g, k, p, &n, &m, &axis, part);
+}
+
+extern "C" size_t dion3_workspace_bytes(const dion3_group* g, int k, const dion3_ns_params* p) {
+  const size_t a = dion3_rowsel_workspace_bytes(g);
+  const size_t b = dion3_gram_ns_workspace_bytes(g, k, p);
+  if (!a || !b) return 0;
+  return a > b ? a : b;
+}
+
+extern "C" int dion3_gram_ns(const dion3_group* g, const void* M, const int32_t* idx, int k,
+                             const dion3_ns_params* p, void* O, void* ws, size_t ws_bytes, void* stream) {
+  int n, m, axis;
+  size_t part[4];
+  const size_t need = gram_group_parts(g, k, p, &n, &m, &axis, part);
+  if (!need || !M || !idx || !O) return DION3_ERR_INVALID_ARG;
+  if (g->dtype != DION3_F32 && g->dtype != DION3_BF16) return DION3_ERR_INVALID_ARG;
+  if (p->T < 1 || !p->coeffs || !(p->eps >= 0.f)) return DION3_ERR_INVALID_ARG;
+  for (int i = 0; i < 3 * p->T; ++i)
+    if (!(p->coeffs[i] == p->coeffs[i])) return DION3_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < need) return DION3_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  double* lines = (double*)w;
+  double* sqn = (double*)(w + part[0]);
+  void* X0 = w + part[0] + part[1];
+  void* scratch = w + part[0] + part[1] + part[2];
+  int st = selected_sqnorm(g, axis, M, idx, k, lines, sqn, s);
+  if (!st) st = dion3_gather_rows(g, M, idx, k, sqn, p->eps, p->ns_dtype, X0, stream);
+  if (!st) st = dion3_gram_ns_gathered(g->batch, k, m, p, X0, O, scratch, part[3], stream);
   return st;
 }
 

@@ -124,6 +124,57 @@ __global__ __launch_bounds__(256) void gather_cols_kernel(
   }
 }
 
+// ------------------------------------------- Frobenius norm of the selection
+// Sum of squares of every selected line, in fp64, one wave per line; lanes
+// accumulate in a fixed order and a butterfly combines them.  Rows: the line
+// is contiguous; columns: lane l reads rows l, l + 64, ... of the column.
+template <typename TS>
+__global__ __launch_bounds__(256) void line_sqsum_kernel(
+    const TS* __restrict__ M, long long bstride, int rows, int cols, int axis,
+    const int32_t* __restrict__ idx, int k, double* __restrict__ out) {
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = blockIdx.x * 4 + wave;
+  if (i >= k) return;
+  const int nlines = axis == 0 ? rows : cols;
+  const int r = idx[(long long)b * k + i];
+  double s = 0.0;
+  if (r >= 0 && r < nlines) {
+    const TS* Mb = M + b * bstride;
+    if (axis == 0) {
+      const TS* src = Mb + (long long)r * cols;
+      for (int c = lane; c < cols; c += 64) {
+        const double v = (double)Store<TS>::to_f32(src[c]);
+        s += v * v;
+      }
+    } else {
+      for (int j = lane; j < rows; j += 64) {
+        const double v = (double)Store<TS>::to_f32(Mb[(long long)j * cols + r]);
+        s += v * v;
+      }
+    }
+  }
+  s = wave_sum(s);
+  if (lane == 0) out[(long long)b * k + i] = s;
+}
+
+// Per matrix, the sum of its k line sums: thread t adds lines t, t + 256, ...
+// in order, then a fixed tree over the threads.
+__global__ __launch_bounds__(256) void sum_lines_kernel(const double* __restrict__ in, int k,
+                                                        double* __restrict__ out) {
+  __shared__ double red[256];
+  const int b = blockIdx.x, t = threadIdx.x;
+  double s = 0.0;
+  for (int i = t; i < k; i += 256) s += in[(long long)b * k + i];
+  red[t] = s;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (t < w) red[t] += red[t + w];
+    __syncthreads();
+  }
+  if (t == 0) out[b] = red[0];
+}
+
 // ------------------------------------------------------------------ apply
 template <typename TS, typename TO, bool VEC>
 __global__ __launch_bounds__(256) void apply_rows_kernel(
@@ -303,6 +354,24 @@ static void launch_apply(const dion3_group* g, int axis, int n, int m, void* W, 
                        g->batch_stride, g->rows, g->cols, idx, k, (const TO*)O, ostride, rs, eta, u,
                        decay, mu);
   }
+}
+
+// ||M[S,:]||_F^2 per matrix into sqn[batch] (fp64), with line_ws [batch][k]
+// fp64 holding the per-line sums.  Arguments are validated by the caller.
+int selected_sqnorm(const dion3_group* g, int axis, const void* M, const int32_t* idx, int k,
+                    double* line_ws, double* sqn, hipStream_t s) {
+  TimedLaunch tl("selected_norm", s);
+  dim3 grid((k + 3) / 4, g->batch);
+  if (g->dtype == DION3_BF16)
+    hipLaunchKernelGGL((line_sqsum_kernel<bf16_t>), grid, dim3(256), 0, s, (const bf16_t*)M, g->batch_stride,
+                       g->rows, g->cols, axis, idx, k, line_ws);
+  else if (g->dtype == DION3_F32)
+    hipLaunchKernelGGL((line_sqsum_kernel<float>), grid, dim3(256), 0, s, (const float*)M, g->batch_stride,
+                       g->rows, g->cols, axis, idx, k, line_ws);
+  else
+    return DION3_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(sum_lines_kernel, dim3(g->batch), dim3(256), 0, s, (const double*)line_ws, k, sqn);
+  return launch_status();
 }
 
 }  // namespace dion3

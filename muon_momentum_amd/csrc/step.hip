@@ -66,7 +66,7 @@ static bool make_plan(int ng, const dion3_group* g, const int* k, const dion3_ns
     const int kk = k[c[0]], mm = P.m[c[0]];
     P.xbuf = std::max(P.xbuf, al256((size_t)nb * kk * mm * es));
     P.gram = std::max(P.gram, mm == kk ? dion3_standard_ns_workspace_bytes(nb, kk, mm, p->ns_dtype)
-                                       : dion3_gram_ns_workspace_bytes(nb, kk, mm, p->ns_dtype));
+                                       : dion3_gram_ns_gathered_workspace_bytes(nb, kk, mm, p->ns_dtype));
   }
   return true;
 }
@@ -118,6 +118,29 @@ static int side_ctx(size_t nev, SideCtx** out) {
   }
   *out = &c;
   return DION3_OK;
+}
+// Destroys the library streams and events of every device (see dion3_release).
+int release_step_resources() {
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  int st = DION3_OK;
+  int prev = -1;
+  for (int d = 0; d < kMaxDevices; ++d) {
+    SideCtx& c = g_side[d];
+    if (!c.side && !c.mem && c.ev.empty()) continue;
+    if (prev < 0 && hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (hipSetDevice(d) != hipSuccess) { st = DION3_ERR_HIP; continue; }
+    // the streams' queued work completes before they are destroyed
+    for (hipStream_t* q : {&c.side, &c.mem}) {
+      if (!*q) continue;
+      if (hipStreamSynchronize(*q) != hipSuccess || hipStreamDestroy(*q) != hipSuccess) st = DION3_ERR_HIP;
+      *q = nullptr;
+    }
+    for (hipEvent_t e : c.ev)
+      if (hipEventDestroy(e) != hipSuccess) st = DION3_ERR_HIP;
+    c.ev.clear();
+  }
+  if (prev >= 0 && hipSetDevice(prev) != hipSuccess) st = DION3_ERR_HIP;
+  return st;
 }
 }  // namespace dion3
 
@@ -235,7 +258,7 @@ static int run_step(int n_groups, const dion3_group* groups, void* const* W, voi
     // aspect ratio 1: standard Newton-Schulz on the symmetric kernels (fewer
     // launches, equal work); otherwise Gram Newton-Schulz
     if (!st) st = mm == kk ? dion3_standard_ns(nb, kk, mm, p, X0buf[c & 1], O, gws, P.gram, side)
-                           : dion3_gram_ns(nb, kk, mm, p, X0buf[c & 1], O, gws, P.gram, side);
+                           : dion3_gram_ns_gathered(nb, kk, mm, p, X0buf[c & 1], O, gws, P.gram, side);
     if (!st) st = hip_ok(hipEventRecord(ev_ns[c], side));
     // the next class's momentum and gather go ahead of this class's update
     // on the overlapped stream, so that they run beside these products

@@ -8,13 +8,16 @@ extension can never fall back to anything else.
 
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
 
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdion3.so")
+# DION3_LIB names another build of the same library (the host sanitizer build
+# of the CPU tests); by default the in-tree libdion3.so
+LIB_PATH = os.environ.get("DION3_LIB") or os.path.join(_HERE, "libdion3.so")
 
 F32, F16, BF16 = 0, 1, 2
 _TORCH_TO_DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
@@ -63,8 +66,12 @@ def _load() -> ctypes.CDLL:
         "dion3_step_deferred": (i, [i, gp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
                                     ctypes.POINTER(i), ctypes.POINTER(vp), i, pp, f, f, f, vp, sz, vp]),
         "dion3_gather_rows": (i, [gp, vp, vp, i, vp, f, i, vp, vp]),
-        "dion3_gram_ns_workspace_bytes": (sz, [i, i, i, i]),
-        "dion3_gram_ns": (i, [i, i, i, pp, vp, vp, vp, sz, vp]),
+        "dion3_gram_ns_gathered_workspace_bytes": (sz, [i, i, i, i]),
+        "dion3_gram_ns_gathered": (i, [i, i, i, pp, vp, vp, vp, sz, vp]),
+        "dion3_gram_ns_workspace_bytes": (sz, [gp, i, pp]),
+        "dion3_workspace_bytes": (sz, [gp, i, pp]),
+        "dion3_gram_ns": (i, [gp, vp, vp, i, pp, vp, vp, sz, vp]),
+        "dion3_release": (i, []),
         "dion3_standard_ns_workspace_bytes": (sz, [i, i, i, i]),
         "dion3_standard_ns": (i, [i, i, i, pp, vp, vp, vp, sz, vp]),
         "dion3_syrk": (i, [i, i, i, i, vp, ll, vp, ll, f, f, vp]),
@@ -91,6 +98,8 @@ def _load() -> ctypes.CDLL:
 
 
 lib = _load()
+# the library's own streams and events go before the HIP runtime shuts down
+atexit.register(lib.dion3_release)
 
 
 # ------------------------------------------------------------------ helpers
@@ -190,17 +199,44 @@ def dion3_gather_rows(M, idx, k, sel_sqnorm, X, eps=DEFAULT_EPS, sel_axis=-1):
                                  dtype_code(X.dtype), _ptr(X), _stream()), "dion3_gather_rows")
 
 
-def dion3_gram_ns_workspace_bytes(batch, k, m, ns_dtype) -> int:
-    return lib.dion3_gram_ns_workspace_bytes(batch, k, m, ns_dtype)
+def dion3_gram_ns_gathered_workspace_bytes(batch, k, m, ns_dtype) -> int:
+    return lib.dion3_gram_ns_gathered_workspace_bytes(batch, k, m, ns_dtype)
 
 
-def dion3_gram_ns(X0, O, params=None, ws=None):
+def dion3_gram_ns_gathered(X0, O, params=None, ws=None):
     b, k, m = X0.shape
     p = params if params is not None else make_ns_params(ns_dtype=dtype_code(X0.dtype))
     if ws is None:
-        ws = workspace(dion3_gram_ns_workspace_bytes(b, k, m, p.ns_dtype), X0.device)
-    _check(lib.dion3_gram_ns(b, k, m, ctypes.byref(p), _ptr(X0), _ptr(O), _ptr(ws), ws.numel(),
-                             _stream()), "dion3_gram_ns")
+        ws = workspace(dion3_gram_ns_gathered_workspace_bytes(b, k, m, p.ns_dtype), X0.device)
+    _check(lib.dion3_gram_ns_gathered(b, k, m, ctypes.byref(p), _ptr(X0), _ptr(O), _ptr(ws), ws.numel(),
+                                      _stream()), "dion3_gram_ns_gathered")
+
+
+def dion3_gram_ns_workspace_bytes(g: Group, k: int, params) -> int:
+    return lib.dion3_gram_ns_workspace_bytes(ctypes.byref(g), k, ctypes.byref(params))
+
+
+def dion3_workspace_bytes(g: Group, k: int, params) -> int:
+    return lib.dion3_workspace_bytes(ctypes.byref(g), k, ctypes.byref(params))
+
+
+def dion3_gram_ns(M, idx, k, O, params=None, ws=None, sel_axis=-1):
+    """Gram Newton-Schulz of the selected submatrices M[b][idx[b], :] of the
+    group tensor M (canonical orientation) into O [batch][k][m]."""
+    g = make_group(M, sel_axis)
+    p = params if params is not None else make_ns_params(ns_dtype=dtype_code(O.dtype))
+    if ws is None:
+        nb = dion3_gram_ns_workspace_bytes(g, k, p)
+        if nb == 0:
+            raise Dion3Error("dion3_gram_ns_workspace_bytes: invalid arguments")
+        ws = workspace(nb, M.device)
+    _check(lib.dion3_gram_ns(ctypes.byref(g), _ptr(M), _ptr(idx), k, ctypes.byref(p), _ptr(O), _ptr(ws),
+                             ws.numel(), _stream()), "dion3_gram_ns")
+
+
+def dion3_release() -> None:
+    """Destroy the library's own streams, events and timing events."""
+    _check(lib.dion3_release(), "dion3_release")
 
 
 def dion3_standard_ns_workspace_bytes(batch, k, m, ns_dtype) -> int:

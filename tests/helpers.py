@@ -60,7 +60,7 @@ def manual_step(d, groups, ks, params, eta, wd, mu, keep=None):
         if k == m:
             d.dion3_standard_ns(X, Ob, params)
         else:
-            d.dion3_gram_ns(X, Ob, params)
+            d.dion3_gram_ns_gathered(X, Ob, params)
         off = 0
         for g in members:
             W, M, G = groups[g]

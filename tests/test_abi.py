@@ -99,13 +99,13 @@ def test_invalid_arguments_rejected_without_launch():
     # gram_ns: k > m, bad params, workspace
     p = d.make_ns_params()
     pp = ctypes.byref(p)
-    wsn = L.dion3_gram_ns_workspace_bytes(2, 64, 128, d.F16)
+    wsn = L.dion3_gram_ns_gathered_workspace_bytes(2, 64, 128, d.F16)
     assert wsn > 0
-    assert L.dion3_gram_ns(2, 129, 128, pp, FAKE, ctypes.c_void_p(0x2000), FAKE, wsn, None) == -1
-    assert L.dion3_gram_ns(2, 64, 128, pp, FAKE, ctypes.c_void_p(0x2000), FAKE, wsn - 1, None) == -3
-    assert L.dion3_gram_ns(2, 64, 128, pp, FAKE, FAKE, FAKE, wsn, None) == -1          # X0 == O
+    assert L.dion3_gram_ns_gathered(2, 129, 128, pp, FAKE, ctypes.c_void_p(0x2000), FAKE, wsn, None) == -1
+    assert L.dion3_gram_ns_gathered(2, 64, 128, pp, FAKE, ctypes.c_void_p(0x2000), FAKE, wsn - 1, None) == -3
+    assert L.dion3_gram_ns_gathered(2, 64, 128, pp, FAKE, FAKE, FAKE, wsn, None) == -1          # X0 == O
     bad = d.make_ns_params(T=0, coeffs=[])
-    assert L.dion3_gram_ns(2, 64, 128, ctypes.byref(bad), FAKE, ctypes.c_void_p(0x2000), FAKE, wsn, None) == -1
+    assert L.dion3_gram_ns_gathered(2, 64, 128, ctypes.byref(bad), FAKE, ctypes.c_void_p(0x2000), FAKE, wsn, None) == -1
     # standard_ns: same argument checks
     wss = L.dion3_standard_ns_workspace_bytes(2, 64, 128, d.F16)
     assert wss > 0
@@ -130,11 +130,11 @@ def test_status_strings():
         assert isinstance(d.lib.dion3_status_string(code), bytes)
 
 
-def test_gram_ns_workspace_formula():
+def test_gram_ns_gathered_workspace_formula():
     L = d.lib
     for (b, k, m, dt, es) in [(3, 100, 300, d.F16, 2), (1, 256, 1024, d.F32, 4)]:
         al = lambda v: (v + 255) // 256 * 256
-        assert L.dion3_gram_ns_workspace_bytes(b, k, m, dt) == al(b * k * m * es) + 4 * al(b * k * k * es)
+        assert L.dion3_gram_ns_gathered_workspace_bytes(b, k, m, dt) == al(b * k * m * es) + 4 * al(b * k * k * es)
 
 
 def test_standard_ns_workspace_formula():
@@ -186,3 +186,42 @@ def test_normuon_entry_points_reject_invalid_arguments():
     assert L.dion3_step_normuon(1, groups, *args, vs, 0, 0, pp, 0.1, 0.0, 0.9, 2.0, 1e-8, FAKE, sw, None) == -1
     assert L.dion3_step_normuon(1, groups, *args, vs, 0, 0, pp, 0.1, 0.0, 0.9, 0.95, 1e-8, FAKE, sw - 1,
                                 None) == -3
+
+
+def test_group_gram_ns_workspace_and_argument_checks():
+    """dion3_workspace_bytes serves both momentum_rowsel and the group form of
+    dion3_gram_ns; the group form rejects invalid arguments before launching."""
+    L = d.lib
+    al = lambda v: (v + 255) // 256 * 256
+    p = d.make_ns_params(ns_dtype=d.F16)
+    pp = ctypes.byref(p)
+    for (r, c, b, k) in [(64, 300, 3, 16), (500, 96, 2, 40), (128, 128, 1, 128)]:
+        g = d.Group(r, c, b, r * c, d.BF16, -1)
+        n, m = min(r, c), max(r, c)
+        want = al(b * k * 8) + al(b * 8) + al(b * k * m * 2) + L.dion3_gram_ns_gathered_workspace_bytes(b, k, m, d.F16)
+        assert L.dion3_gram_ns_workspace_bytes(ctypes.byref(g), k, pp) == want
+        assert L.dion3_workspace_bytes(ctypes.byref(g), k, pp) == max(want, L.dion3_rowsel_workspace_bytes(ctypes.byref(g)))
+    g = d.Group(64, 300, 2, 64 * 300, d.BF16, -1)
+    gp = ctypes.byref(g)
+    P2 = ctypes.c_void_p(0x2000)
+    ws = L.dion3_gram_ns_workspace_bytes(gp, 16, pp)
+    assert L.dion3_gram_ns_workspace_bytes(gp, 0, pp) == 0
+    assert L.dion3_gram_ns_workspace_bytes(gp, 65, pp) == 0                     # k > n
+    assert L.dion3_workspace_bytes(gp, 65, pp) == 0
+    assert L.dion3_gram_ns(gp, None, FAKE, 16, pp, P2, FAKE, ws, None) == -1    # M missing
+    assert L.dion3_gram_ns(gp, FAKE, None, 16, pp, P2, FAKE, ws, None) == -1    # idx missing
+    assert L.dion3_gram_ns(gp, FAKE, FAKE, 16, pp, None, FAKE, ws, None) == -1  # O missing
+    assert L.dion3_gram_ns(gp, FAKE, FAKE, 0, pp, P2, FAKE, ws, None) == -1
+    assert L.dion3_gram_ns(gp, FAKE, FAKE, 16, pp, P2, FAKE, ws - 1, None) == -3
+    assert L.dion3_gram_ns(gp, FAKE, FAKE, 16, pp, P2, None, ws, None) == -3
+    bad = d.make_ns_params(T=0, coeffs=[])
+    assert L.dion3_gram_ns(gp, FAKE, FAKE, 16, ctypes.byref(bad), P2, FAKE, ws, None) == -1
+    g16 = d.Group(64, 300, 2, 64 * 300, d.F16, -1)                             # storage must be bf16 / f32
+    assert L.dion3_gram_ns(ctypes.byref(g16), FAKE, FAKE, 16, pp, P2, FAKE, ws, None) == -1
+
+
+def test_release_without_gpu_work_is_a_no_op():
+    """dion3_release frees only what the library created; with nothing created
+    it makes no HIP call and succeeds (twice in a row as well)."""
+    assert d.lib.dion3_release() == 0
+    assert d.lib.dion3_release() == 0

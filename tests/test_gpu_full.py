@@ -5,10 +5,10 @@ classes, same kernels and grids).
 The oracle runs the whole step on sampled matrices of every group: selected
 indices and M bit for bit, the W update bit for bit given the GPU's
 Newton-Schulz output O, and O within the fp16 tolerance (3e-2 relative
-Frobenius).  On the first step every eighth matrix of every group is also
-checked for a property that holds at any size: the selected lines are those
-of largest l1 norm (ties to the lower index), norms recomputed on the host
-from the step's input momentum (M0 = 0, so that momentum is G)."""
+Frobenius), printed next to the extreme singular values of the normalised
+input.  On the first step every eighth matrix of every group is also checked
+against the oracle's selection from exact l1 norms of the step's momentum
+(M0 = 0, so that momentum is G)."""
 
 import math
 
@@ -30,19 +30,10 @@ def d():
     return mod
 
 
-def check_selection_property(Mc, idx, k):
-    """idx (ascending) holds the k lines of largest l1 norm, ties to lower index."""
-    keys = np.abs(Mc).sum(axis=1)
-    n = keys.shape[0]
-    assert idx.shape == (k,) and np.all(np.diff(idx) > 0) and idx[0] >= 0 and idx[-1] < n
-    if k == n:
-        return
-    sel = np.zeros(n, dtype=bool)
-    sel[idx] = True
-    lo, hi = keys[sel].min(), keys[~sel].max()
-    assert lo >= hi
-    if lo == hi:   # a tie at the boundary: tied unselected lines come after the tied selected ones
-        assert np.where(~sel & (keys == hi))[0].min() > np.where(sel & (keys == lo))[0].max()
+def check_selection(Mc, idx, k):
+    """idx equals the oracle's selection from the exact l1 norms of Mc."""
+    from oracle_pool import exact_l1
+    assert np.array_equal(idx, O.select_rows(exact_l1(Mc), k))
 
 
 def run_set(d, name, f, steps, sample, prop_every=8):
@@ -73,7 +64,7 @@ def run_set(d, name, f, steps, sample, prop_every=8):
             if step == 0:
                 for j in range(0, b, prop_every):
                     Gc = to64(tensors[gi][2][j])
-                    check_selection_property(Gc if ax == 0 else Gc.T, idx_all[j], ks[gi])
+                    check_selection(Gc if ax == 0 else Gc.T, idx_all[j], ks[gi])
             for j in sample.get(gi, []):
                 Wh, Mh = state[(gi, j)]
                 out = O.dion3_step(Wh, Mh, Gh[(gi, j)], k=ks[gi], mu=mu, eta=eta, fmt="bf16")
@@ -82,9 +73,14 @@ def run_set(d, name, f, steps, sample, prop_every=8):
                 assert np.array_equal(bits(tensors[gi][1][j]), np_bits(out["M"], torch.bfloat16)), where
                 Og = to64(Os[gi][j])
                 err = rel_fro(Og, out["O"])
+                Mc = O.momentum_accumulate(Mh, Gh[(gi, j)], "bf16")
+                # conditioning of the Newton-Schulz input next to every error figure
+                X0 = O.frobenius_normalize((Mc if ax == 0 else Mc.T)[out["idx"]])
+                sv = np.linalg.svd(X0, compute_uv=False)
+                print(f"# {where}: O rel err {err:.3e}, X0 sigma_min {sv[-1]:.3e} sigma_max {sv[0]:.3e} "
+                      f"(ratio {sv[-1] / sv[0]:.3e})", flush=True)
                 worst = max(worst, err)
                 assert err <= 3e-2, (where, err)
-                Mc = O.momentum_accumulate(Mh, Gh[(gi, j)], "bf16")
                 Wc, Mcc = (Wpre[(gi, j)], Mc) if ax == 0 else (Wpre[(gi, j)].T, Mc.T)
                 Wg, _ = O.apply_rows(Wc, Mcc, out["idx"], Og, eta, 0.0, mu, "bf16")
                 if ax == 1:

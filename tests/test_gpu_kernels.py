@@ -233,7 +233,7 @@ def test_gram_ns(d, xdt, tol, b, k, m):
     Xd = torch.from_numpy(X0).to(TD[xdt]).to(DEV)
     Od = torch.empty_like(Xd)
     params = d.make_ns_params(ns_dtype=d.dtype_code(TD[xdt]))
-    d.dion3_gram_ns(Xd, Od, params)
+    d.dion3_gram_ns_gathered(Xd, Od, params)
     torch.cuda.synchronize()
     xin = to64(Xd)
     for i in range(b):
@@ -244,6 +244,46 @@ def test_gram_ns(d, xdt, tol, b, k, m):
             assert err <= 1e-2   # the fp16 storage model predicts about 1e-3
 
 
+@pytest.mark.parametrize("dt,xdt,tol", [("bf16", "f16", 3e-2), ("f32", "f32", 1e-4), ("bf16", "f32", 1e-4)])
+@pytest.mark.parametrize("rows,cols,batch,f", [(300, 1000, 2, 0.25), (600, 200, 2, 0.25), (256, 1024, 1, 1.0),
+                                               (1100, 520, 1, 0.5)])
+def test_gram_ns_group_form(d, dt, xdt, tol, rows, cols, batch, f):
+    """dion3_gram_ns in its (group, M, idx, k) form: the selected submatrix is
+    normalised and orthogonalised like the oracle's step (Section 2, Section
+    4), and agrees with momentum_rowsel + gather + the gathered form."""
+    n = min(rows, cols)
+    k = O.k_from_fraction(n, f)
+    M, Mh, Gh, idx, keys, sqn, ax = _rowsel_case(d, rows, cols, batch, dt, k)
+    m = cols if ax == 0 else rows
+    idx_d = torch.from_numpy(idx).to(DEV)
+    params = d.make_ns_params(ns_dtype=d.dtype_code(TD[xdt]))
+    Og = torch.empty(batch, k, m, dtype=TD[xdt], device=DEV)
+    d.dion3_gram_ns(M, idx_d, k, Og, params)
+    X = torch.empty(batch, k, m, dtype=TD[xdt], device=DEV)
+    Ox = torch.empty_like(X)
+    d.dion3_gather_rows(M, idx_d, k, torch.from_numpy(sqn).to(DEV), X, eps=params.eps)
+    d.dion3_gram_ns_gathered(X, Ox, params)
+    torch.cuda.synchronize()
+    for b in range(batch):
+        Mc = to64(M[b]) if ax == 0 else to64(M[b]).T
+        ref = O.ns_gram(Mc[idx[b]])
+        assert rel_fro(to64(Og[b]), ref) <= tol
+        # same normalised input up to the last bit of the fp64 norm: the two
+        # forms agree far inside the tolerance
+        assert rel_fro(to64(Og[b]), to64(Ox[b])) <= (2e-3 if xdt == "f16" else 1e-6)
+
+
+def test_gram_ns_group_form_zero_selection(d):
+    """An all-zero selected submatrix gives O = 0 (the eps guard of the
+    normalisation)."""
+    M = torch.zeros(2, 64, 200, dtype=torch.bfloat16, device=DEV)
+    idx = torch.arange(16, dtype=torch.int32, device=DEV).repeat(2, 1)
+    Og = torch.full((2, 16, 200), 7.0, dtype=torch.float16, device=DEV)
+    d.dion3_gram_ns(M, idx, 16, Og, d.make_ns_params(ns_dtype=d.F16))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(Og).item() == 0
+
+
 def test_gram_ns_restart_variants(d):
     b, k, m = 1, 128, 512
     rng = np.random.default_rng(1)
@@ -251,7 +291,7 @@ def test_gram_ns_restart_variants(d):
     Xd = torch.from_numpy(X0[None]).float().to(DEV)
     for mask, restart in [(0, ()), (1 << 2, (2,)), ((1 << 1) | (1 << 3), (1, 3)), ((1 << 1) | (1 << 2) | (1 << 3) | (1 << 4), (1, 2, 3, 4))]:
         Od = torch.empty_like(Xd)
-        d.dion3_gram_ns(Xd, Od, d.make_ns_params(restart_mask=mask, ns_dtype=d.F32))
+        d.dion3_gram_ns_gathered(Xd, Od, d.make_ns_params(restart_mask=mask, ns_dtype=d.F32))
         torch.cuda.synchronize()
         ref = O.ns_gram(to64(Xd)[0], restart_after=restart, eps=0.0)
         assert rel_fro(to64(Od)[0], ref) <= 1e-4, mask
@@ -305,7 +345,7 @@ def test_gemm_deterministic(d):
 # (k = 1024 and 1280 selected lines, m up to 11008), large enough that the
 # library takes its 256 x 256 tile.  Every matrix is checked for exact
 # symmetry; a sample of matrices is compared with fp64 products.  (The
-# library picks the large tile when a launch has at least 512 of them.)
+# library picks the large tile when a launch has at least 128 of them.)
 def _sample(b):
     return sorted({0, b // 2, b - 1})
 

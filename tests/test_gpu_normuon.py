@@ -128,7 +128,7 @@ def _manual_normuon(d, groups, Vs, ks, params, eta, mu, beta2, eps):
         if k == m:
             d.dion3_standard_ns(X, Ob, params)
         else:
-            d.dion3_gram_ns(X, Ob, params)
+            d.dion3_gram_ns_gathered(X, Ob, params)
         off = 0
         for g in members:
             W, M, G = groups[g]

@@ -191,3 +191,79 @@ def test_momentum_ef_against_oracle(d):
             ref = O.momentum_accumulate(dec, Gc, "bf16")
             ref = ref if axis == 0 else ref.T
             assert np.array_equal(bits(M[b]), np_bits(ref, torch.bfloat16)), (rows, cols, b)
+
+
+def test_zero_gradient_step_leaves_w(d):
+    """A matrix whose momentum and gradient are zero: every key is 0, so the
+    first k lines are selected (ties to the lower index), the selected
+    submatrix is zero, O = 0 (the eps guard of the normalisation) and W is
+    unchanged bit for bit; its batch neighbours are updated as usual."""
+    shapes = [(128, 512, 3), (512, 128, 2)]
+    ks = [32, 32]
+    params = d.make_ns_params(ns_dtype=d.F16)
+    A = _groups(shapes, "bf16", step=4, seed0=60)
+    for W, M, G in A:
+        M[1].zero_()
+        G[1].zero_()
+    W0 = [W.clone() for W, _, _ in A]
+    idx = [torch.empty(b, k, dtype=torch.int32, device=DEV) for (_, _, b), k in zip(shapes, ks)]
+    plan = d.StepPlan([g[0] for g in A], [g[1] for g in A], [g[2] for g in A], ks, idx, params)
+    plan.step(0.04, 0.0, 0.95)
+    torch.cuda.synchronize()
+    for gi, (W, M, G) in enumerate(A):
+        assert np.array_equal(idx[gi][1].cpu().numpy(), np.arange(ks[gi]))
+        assert np.array_equal(bits(W[1]), bits(W0[gi][1])), gi
+        assert torch.count_nonzero(M[1]).item() == 0
+        assert not np.array_equal(bits(W[0]), bits(W0[gi][0])), gi
+
+
+def test_resume_round_trip_matches_straight_run(d):
+    """Checkpoint and resume: three deferred steps in a row equal one deferred
+    step, completion of its pending decay, a host round trip of W and M (the
+    whole optimizer state besides the step count), and two more deferred
+    steps (the first with no pending decay).  Indices, W and, once the last
+    decay is completed, M agree bit for bit."""
+    shapes = [(128, 512, 3), (512, 128, 2), (256, 256, 2)]
+    dt, mu, eta = "bf16", 0.95, 0.04
+    params = d.make_ns_params(ns_dtype=d.F16)
+    ks = [d.dion3_k_from_fraction(min(r, c), 0.25) for r, c, _ in shapes]
+    A = _groups(shapes, dt, step=0, seed0=70)
+    B = [(W.clone(), M.clone(), G.clone()) for W, M, G in A]
+    idx_a = [torch.empty(b, k, dtype=torch.int32, device=DEV) for (_, _, b), k in zip(shapes, ks)]
+    idx_b = [t.clone() for t in idx_a]
+    pa = d.StepPlan([g[0] for g in A], [g[1] for g in A], [g[2] for g in A], ks, idx_a, params)
+    pb = d.StepPlan([g[0] for g in B], [g[1] for g in B], [g[2] for g in B], ks, idx_b, params)
+
+    def grads(step):
+        for gi, (r, c, b) in enumerate(shapes):
+            Gn = synth.gradient(r, c, b, dtype=dt, device=DEV, group_seed=70 + gi, step=step + 1)
+            A[gi][2].copy_(Gn)
+            B[gi][2].copy_(Gn)
+
+    grads(0)
+    pa.step_deferred(eta, 0.0, mu, has_prev=False)
+    pb.step_deferred(eta, 0.0, mu, has_prev=False)
+    # checkpoint of B: complete the pending decay, save W and M on the host,
+    # scribble over the device state, restore it
+    pb.flush_decay(mu)
+    torch.cuda.synchronize()
+    saved = [(W.cpu().clone(), M.cpu().clone()) for W, M, _ in B]
+    for W, M, _ in B:
+        W.fill_(float("nan"))
+        M.fill_(float("nan"))
+    for (W, M, _), (Ws, Ms) in zip(B, saved):
+        W.copy_(Ws.to(DEV))
+        M.copy_(Ms.to(DEV))
+    for step in (1, 2):
+        grads(step)
+        pa.step_deferred(eta, 0.0, mu, has_prev=True)
+        pb.step_deferred(eta, 0.0, mu, has_prev=step > 1)   # the restored M owes no decay
+        torch.cuda.synchronize()
+        for gi in range(len(shapes)):
+            assert torch.equal(idx_a[gi], idx_b[gi]), (step, gi)
+            assert np.array_equal(bits(A[gi][0]), bits(B[gi][0])), (step, gi)
+    pa.flush_decay(mu)
+    pb.flush_decay(mu)
+    torch.cuda.synchronize()
+    for gi in range(len(shapes)):
+        assert np.array_equal(bits(A[gi][1]), bits(B[gi][1])), gi
