@@ -44,7 +44,8 @@ enum {
   DION3_ERR_INVALID_ARG = -1,   /* null pointer, size <= 0, k outside [1, n], bad dtype */
   DION3_ERR_UNSUPPORTED = -2,   /* valid but not implemented (e.g. n > 32768 in top-k) */
   DION3_ERR_WORKSPACE = -3,     /* workspace missing or smaller than required */
-  DION3_ERR_HIP = -4            /* a HIP launch or runtime call failed */
+  DION3_ERR_HIP = -4,           /* a HIP launch or runtime call failed */
+  DION3_ERR_TOO_LARGE = -5      /* needs more than the fixed scratch of a no-allocation entry point */
 };
 
 /* A batch of same-shape matrices (W, G and M share this description). */
@@ -118,6 +119,23 @@ int dion3_momentum_rowsel_ef(const dion3_group* g, void* M, const void* G, int k
                              int32_t* idx, double* keys, double* sel_sqnorm,
                              const int32_t* prev_idx, int prev_k, float mu,
                              void* ws, size_t ws_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): exactly
+ * dion3_momentum_rowsel_ef, with its scratch (the per-line partial sums of
+ * the selection) in a fixed per-GPU array of DION3_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) inside the library instead of a caller's workspace.  Nothing is
+ * allocated, freed or cleared by the call; the array is set up on the first
+ * call on each device (its address looked up while that device is current)
+ * and held until the process ends.  A group whose
+ * dion3_rowsel_workspace_bytes exceeds the array returns DION3_ERR_TOO_LARGE
+ * before anything is launched (split the batch).  Every call on one GPU uses
+ * the same array: calls that may overlap on one GPU (on different streams,
+ * or from different threads) race and must be ordered by the caller. */
+#define DION3_NOALLOC_SCRATCH_BYTES (64ull << 20)
+int dion3_momentum_rowsel_noalloc(const dion3_group* g, void* M, const void* G, int k,
+                                  int32_t* idx, double* keys, double* sel_sqnorm,
+                                  const int32_t* prev_idx, int prev_k, float mu, void* stream);
 
 /* ------------------------------------------------------- gather + scale */
 

@@ -17,6 +17,7 @@ extern "C" const char* dion3_status_string(int status) {
     case DION3_ERR_UNSUPPORTED: return "unsupported";
     case DION3_ERR_WORKSPACE: return "workspace missing or too small";
     case DION3_ERR_HIP: return "HIP error";
+    case DION3_ERR_TOO_LARGE: return "input needs more than the fixed scratch of the no-allocation entry point";
   }
   return "unknown status";
 }

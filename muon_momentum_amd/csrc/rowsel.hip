@@ -18,6 +18,8 @@
 // toward lower indices with an ordered prefix count, and compacts the selected
 // indices in ascending order.  Every reduction has a fixed order, so results
 // are bitwise reproducible.
+#include <mutex>
+
 #include "common.h"
 
 namespace dion3 {
@@ -432,4 +434,51 @@ extern "C" int dion3_momentum_rowsel(const dion3_group* g, void* M, const void* 
                                      void* ws, size_t ws_bytes, void* stream) {
   return dion3_momentum_rowsel_ef(g, M, G, k, idx, keys, sel_sqnorm, nullptr, 0, 0.f, ws, ws_bytes,
                                   stream);
+}
+
+// ------------------------------------------- the entry point that allocates nothing
+// The top-k partial sums of dion3_momentum_rowsel_noalloc live in this fixed
+// array instead of a caller's workspace.  Each GPU holds its own copy until
+// the process ends; host code never passes the array's name to a kernel (on
+// the host it is only a stand-in), but the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device on the first call there.  Every partial sum is written before it is
+// read, so nothing needs clearing between calls.
+static __device__ __align__(256) char scratch[DION3_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kScratchDevices];   // per device: its copy of `scratch`
+}  // namespace
+
+static int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return DION3_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DION3_ERR_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return DION3_OK;
+}
+
+extern "C" int dion3_momentum_rowsel_noalloc(const dion3_group* g, void* M, const void* G, int k,
+                                             int32_t* idx, double* keys, double* sel_sqnorm,
+                                             const int32_t* prev_idx, int prev_k, float mu,
+                                             void* stream) {
+  int n, m, axis;
+  if (!canonical_dims(g, &n, &m, &axis)) return DION3_ERR_INVALID_ARG;
+  if (!M || !G || !idx || k < 1 || k > n) return DION3_ERR_INVALID_ARG;
+  if (prev_idx && (prev_k < 1 || prev_k > n)) return DION3_ERR_INVALID_ARG;
+  if (g->dtype != DION3_F32 && g->dtype != DION3_BF16) return DION3_ERR_INVALID_ARG;
+  if (n > kTopkThreads * kTopkPer) return DION3_ERR_UNSUPPORTED;
+  if (dion3_rowsel_workspace_bytes(g) > (size_t)DION3_NOALLOC_SCRATCH_BYTES) return DION3_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  const int st = scratch_address(&ws);
+  if (st) return st;
+  return dion3_momentum_rowsel_ef(g, M, G, k, idx, keys, sel_sqnorm, prev_idx, prev_k, mu, ws,
+                                  (size_t)DION3_NOALLOC_SCRATCH_BYTES, stream);
 }

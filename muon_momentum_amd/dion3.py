@@ -63,6 +63,7 @@ def _load() -> ctypes.CDLL:
         "dion3_momentum_rowsel": (i, [gp, vp, vp, i, vp, vp, vp, vp, sz, vp]),
         "dion3_momentum_rowsel_ef": (i, [gp, vp, vp, i, vp, vp, vp, vp, i, f, vp, sz, vp]),
         "dion3_decay_rows": (i, [gp, vp, vp, i, f, vp]),
+        "dion3_momentum_rowsel_noalloc": (i, [gp, vp, vp, i, vp, vp, vp, vp, i, f, vp]),
         "dion3_step_deferred": (i, [i, gp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
                                     ctypes.POINTER(i), ctypes.POINTER(vp), i, pp, f, f, f, vp, sz, vp]),
         "dion3_gather_rows": (i, [gp, vp, vp, i, vp, f, i, vp, vp]),
@@ -186,6 +187,16 @@ def dion3_momentum_rowsel_ef(M, G, k, idx, prev_idx, prev_k, mu, keys=None, sel_
     _check(lib.dion3_momentum_rowsel_ef(ctypes.byref(g), _ptr(M), _ptr(G), k, _ptr(idx), _ptr(keys),
                                         _ptr(sel_sqnorm), _ptr(prev_idx), prev_k, mu, _ptr(ws), ws.numel(),
                                         _stream()), "dion3_momentum_rowsel_ef")
+
+
+def dion3_momentum_rowsel_noalloc(M, G, k, idx, keys=None, sel_sqnorm=None, prev_idx=None, prev_k=0, mu=0.0,
+                                  sel_axis=-1):
+    """dion3_momentum_rowsel_ef with the library's fixed per-GPU scratch
+    instead of a workspace (no allocation, no workspace argument)."""
+    g = make_group(M, sel_axis)
+    _check(lib.dion3_momentum_rowsel_noalloc(ctypes.byref(g), _ptr(M), _ptr(G), k, _ptr(idx), _ptr(keys),
+                                             _ptr(sel_sqnorm), _ptr(prev_idx), prev_k, mu, _stream()),
+           "dion3_momentum_rowsel_noalloc")
 
 
 def dion3_decay_rows(M, idx, k, mu, sel_axis=-1):
