@@ -39,6 +39,40 @@ MU = 0.95
 ETA0 = 0.02                      # eta at f = 1; eta = ETA0 / sqrt(f)
 
 
+# Single products at the shapes the measurements cite, for rocprofv3 counter
+# passes (bench.py --probe NAME): description, and a function that builds the
+# operands and returns the launch.
+def _probe_syrk(n):
+    def make(d, synth, torch):
+        A = synth.dense(n, n, 1, dtype="f16", device="cuda:0", seed=1)
+        C = torch.empty(1, n, n, dtype=torch.float16, device="cuda:0")
+        return lambda: d.dion3_syrk(A, C)
+    return make
+
+
+def _probe_qx(d, synth, torch):
+    Q = synth.symmetric(1024, 128, dtype="f16", device="cuda:0", seed=3)
+    X = synth.dense(1024, 4096, 128, dtype="f16", device="cuda:0", seed=4)
+    Y = torch.empty_like(X)
+    return lambda: d.dion3_gemm(Q, X, Y)
+
+
+def _probe_symmul(d, synth, torch):
+    A = synth.symmetric(1024, 128, dtype="f16", device="cuda:0", seed=5)
+    B = synth.symmetric(1024, 128, dtype="f16", device="cuda:0", seed=6)
+    C = torch.empty_like(A)
+    return lambda: d.dion3_sym_mul(A, B, C)
+
+
+PROBES = {
+    "syrk8192": ("C = A A^T, one 8192 x 8192 fp16 A", _probe_syrk(8192)),
+    "syrk4096": ("C = A A^T, one 4096 x 4096 fp16 A", _probe_syrk(4096)),
+    "qx": ("Y = Q X, 128 x (1024 x 1024 by 1024 x 4096) fp16 (the 7B set's first class at f = 1/4)",
+           _probe_qx),
+    "symmul": ("C = A B, 128 x 1024 x 1024 symmetric fp16 (the same class's k x k products)", _probe_symmul),
+}
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -52,6 +86,10 @@ def parse():
                     help="steps of the separate instrumented pass that gives the per-kernel table")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-microbench", action="store_true")
+    ap.add_argument("--probe", choices=list(PROBES), default=None,
+                    help="run a few launches of one product and exit (for hardware counters): "
+                         + "; ".join(f"{k}: {v[0]}" for k, v in PROBES.items()))
+    ap.add_argument("--probe-reps", type=int, default=3)
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size "
                          "reference for hardware byte counters)")
@@ -307,6 +345,14 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+
+    if args.probe:
+        fn = PROBES[args.probe][1](d, synth, torch)
+        for _ in range(args.probe_reps):
+            fn()
+        torch.cuda.synchronize()
+        print(f"# probe {args.probe} done ({args.probe_reps} launches)", file=sys.stderr, flush=True)
+        return
 
     if args.copy_ref_mib > 0:
         nb = args.copy_ref_mib << 20
