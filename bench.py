@@ -86,6 +86,7 @@ def parse():
                     help="steps of the separate instrumented pass that gives the per-kernel table")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-microbench", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the step-graph leg")
     ap.add_argument("--probe", choices=list(PROBES), default=None,
                     help="run a few launches of one product and exit (for hardware counters): "
                          + "; ".join(f"{k}: {v[0]}" for k, v in PROBES.items()))
@@ -258,6 +259,33 @@ def run_step_bench(d, synth, torch, args):
            "p90": per_step[min(len(per_step) - 1, int(math.ceil(0.9 * len(per_step))) - 1)]}
     print(f"# timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
 
+    # the same step as one HIP graph (dion3_step_graph_create): enqueue time of
+    # one launch and K launches timed as above
+    if args.flavor == "muon" and not args.no_graph:
+        graph = plan.graph(eta, 0.0, MU, has_prev=True)
+        for _ in range(3):
+            graph.launch()
+        ghost = []
+        for _ in range(5):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            graph.launch()
+            ghost.append(1e3 * (time.perf_counter() - t0))
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i in range(args.steps):
+            graph.launch()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        gper = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+        pct["graph"] = {"ms_per_step": round(ev[0].elapsed_time(ev[-1]) / args.steps, 3),
+                        "ms_per_step_p50": round(gper[len(gper) // 2], 3),
+                        "host_ms_per_step": round(sorted(ghost)[len(ghost) // 2], 3)}
+        graph.destroy()
+        torch.cuda.synchronize()
+        print(f"# graph {args.steps} steps: {pct['graph']['ms_per_step']:.3f} ms/step", file=sys.stderr,
+              flush=True)
+
     # a separate instrumented pass for the per-kernel table: a HIP event pair
     # around every library launch, on the stream of the launch
     nprof = max(1, min(args.steps, args.profile_steps))
@@ -391,6 +419,7 @@ def main():
         "host_ms_per_step": round(pct["host"], 3),
         "ms_per_step_instrumented": round(pct["instrumented"], 3),
         "profile_steps": pct["profile_steps"],
+        "graph": pct.get("graph"),
         "data": "synthetic (Gaussian gradients with log-normal line scales, seeded)",
         "config": {"workload": f"{args.set} shape set Dion3 step, f={args.f:g}"
                                + ("" if args.flavor == "muon" else ", NorMuon flavour"),

@@ -321,6 +321,28 @@ int dion3_step_deferred(int n_groups, const dion3_group* groups, void* const* W,
                         const dion3_ns_params* p, float eta, float wd, float mu,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* The deferred step as a HIP graph (Section 6: the step's launches have the
+ * same dependencies every step, so one recorded graph replaces them; the
+ * pages replay it to cut the host time per step).  The graph is built node by
+ * node, not by stream capture: every launch of dion3_step_deferred with these
+ * arguments becomes a kernel node, and the order its streams and events give
+ * becomes node dependencies.  It is instantiated once; each dion3_graph_launch
+ * then performs exactly that step (same pointers, scalars and has_prev; the
+ * buffers' current contents) on `stream`, ordered like any other work there,
+ * with one host call.  Creation allocates the graph; launching allocates
+ * nothing.  Results are bit-identical to the eager call.  A graph must not
+ * be launched while another launch of it, or an eager step on the same
+ * tensors or workspace, may run concurrently.  Steady state: run the first
+ * step eagerly (has_prev = 0), then launch a graph created with has_prev = 1
+ * every step. */
+typedef struct dion3_graph_s* dion3_graph;
+int dion3_step_graph_create(int n_groups, const dion3_group* groups, void* const* W, void* const* M,
+                            const void* const* G, const int* k, int32_t* const* idx, int has_prev,
+                            const dion3_ns_params* p, float eta, float wd, float mu,
+                            void* ws, size_t ws_bytes, dion3_graph* out);
+int dion3_graph_launch(dion3_graph g, void* stream);
+int dion3_graph_destroy(dion3_graph g);
+
 /* The whole step in the NorMuon flavour: dion3_step (deferred = 0) or
  * dion3_step_deferred (deferred = 1, has_prev as there) with
  * dion3_normuon_scale before each group's update.  V[i] is group i's

@@ -60,7 +60,7 @@ Timing g_timing;
 namespace dion3 {
 void timing_begin(const char* name, hipStream_t s) {
   Timing& T = g_timing;
-  if (T.cap == 0 || T.used >= T.cap) return;
+  if (T.cap == 0 || T.used >= T.cap || graph_builder()) return;   // no events inside a step graph
   if (hipEventRecord(T.ev[2 * T.used], s) != hipSuccess) return;
   T.name[T.used] = name;
   T.open = true;

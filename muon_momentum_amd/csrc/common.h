@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
 #include "dion3.h"
 
 namespace dion3 {
@@ -108,7 +111,35 @@ struct TimedLaunch {
   ~TimedLaunch() { timing_end(s); }
 };
 
+// ------------------------------------------------------------------ launches
+// Every kernel of the library goes through launch(): eagerly onto the stream,
+// or, while a step graph is being built on this thread (graph.hip), as a
+// kernel node of that graph, the stream standing for a branch of it.  The
+// arguments are converted to the kernel's parameter types and passed by
+// address, the form both hipLaunchKernel and hipGraphAddKernelNode take.
+struct GraphBuilder;
+GraphBuilder* graph_builder();                 // this thread's builder, or nullptr
+int graph_add_kernel(GraphBuilder* b, const void* func, dim3 grid, dim3 block, void** args, hipStream_t s);
+int graph_status(GraphBuilder* b);
+
+template <typename... P, typename... A, size_t... I>
+inline int launch_args(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t s, std::index_sequence<I...>,
+                       A&&... a) {
+  std::tuple<P...> t(static_cast<P>(std::forward<A>(a))...);
+  void* args[] = {(void*)&std::get<I>(t)...};
+  if (GraphBuilder* b = graph_builder()) return graph_add_kernel(b, (const void*)kernel, grid, block, args, s);
+  return hipLaunchKernel((const void*)kernel, grid, block, args, 0, s) == hipSuccess ? DION3_OK : DION3_ERR_HIP;
+}
+template <typename... P, typename... A>
+inline int launch(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t s, A&&... a) {
+  static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+  return launch_args(kernel, grid, block, s, std::index_sequence_for<P...>{}, std::forward<A>(a)...);
+}
+
+// Status of the launches since the last check (the graph being built, or the
+// last HIP error of this thread).
 inline int launch_status() {
+  if (GraphBuilder* b = graph_builder()) return graph_status(b);
   return hipGetLastError() == hipSuccess ? DION3_OK : DION3_ERR_HIP;
 }
 
@@ -128,6 +159,15 @@ inline bool canonical_dims(const dion3_group* g, int* n, int* m, int* axis) {
 
 // Destroys the streams and events the whole-step driver created (step.hip).
 int release_step_resources();
+
+// The deferred whole step (step.hip), and the event record / stream wait it
+// uses: HIP calls, or graph dependencies while a step graph is built (graph.hip).
+int run_step_deferred(int n_groups, const dion3_group* groups, void* const* W, void* const* M,
+                      const void* const* G, const int* k, int32_t* const* idx, int has_prev,
+                      const dion3_ns_params* p, float eta, float wd, float mu, void* ws, size_t ws_bytes,
+                      void* stream);
+int event_record(hipEvent_t e, hipStream_t s);
+int stream_wait(hipStream_t s, hipEvent_t e);
 
 // ||M[S,:]||_F^2 of every matrix of a group (scatter.hip); line_ws holds
 // [batch][k] fp64 per-line sums.

@@ -1175,14 +1175,14 @@ static int launch_typed(const GemmArgs& a, hipStream_t s) {
       if constexpr (OP == OP_SYRK) sym_mul_kernel = a.E == nullptr;
       if constexpr (OP == OP_SYRK)
         if (sym_mul_kernel)
-          hipLaunchKernelGGL((gemm256_kernel<T, TO, OP_SYM_MUL, kStages>), dim3((unsigned)wgs), dim3(kThreads), 0, s, p);
+          (void)launch((gemm256_kernel<T, TO, OP_SYM_MUL, kStages>), dim3((unsigned)wgs), dim3(kThreads), s, p);
       if (!sym_mul_kernel)
-        hipLaunchKernelGGL((gemm256_kernel<T, TO, OP, kStages>), dim3((unsigned)wgs), dim3(kThreads), 0, s, p);
+        (void)launch((gemm256_kernel<T, TO, OP, kStages>), dim3((unsigned)wgs), dim3(kThreads), s, p);
     }
   } else if (fast_for(BM))
-    hipLaunchKernelGGL((gemm_kernel<T, TO, OP, false, BM>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+    (void)launch((gemm_kernel<T, TO, OP, false, BM>), dim3((unsigned)grid), dim3(kThreads), s, p);
   else
-    hipLaunchKernelGGL((gemm_kernel<T, TO, OP, true, BM>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+    (void)launch((gemm_kernel<T, TO, OP, true, BM>), dim3((unsigned)grid), dim3(kThreads), s, p);
   return launch_status();
 }
 

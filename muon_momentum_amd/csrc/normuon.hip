@@ -107,10 +107,10 @@ static void launch_normuon(const dion3_group* g, int n, int m, const int32_t* id
                    (g->batch == 1 || ostride % (16 / (int)sizeof(TO)) == 0);
   dim3 grid((k + 3) / 4, g->batch);
   if (vec)
-    hipLaunchKernelGGL((row_sqsum_kernel<TO, true>), grid, dim3(256), 0, s, (const TO*)O, ostride, k, m, rs);
+    (void)launch((row_sqsum_kernel<TO, true>), grid, dim3(256), s, (const TO*)O, ostride, k, m, rs);
   else
-    hipLaunchKernelGGL((row_sqsum_kernel<TO, false>), grid, dim3(256), 0, s, (const TO*)O, ostride, k, m, rs);
-  hipLaunchKernelGGL(normuon_scale_kernel, dim3(g->batch), dim3(256), 0, s, idx, k, m, V, n, beta2, eps, rs);
+    (void)launch((row_sqsum_kernel<TO, false>), grid, dim3(256), s, (const TO*)O, ostride, k, m, rs);
+  (void)launch(normuon_scale_kernel, dim3(g->batch), dim3(256), s, idx, k, m, V, n, beta2, eps, rs);
 }
 
 }  // namespace dion3

@@ -370,20 +370,16 @@ static void launch_momentum(const dion3_group* g, int axis, void* M, const void*
   if (axis == 0) {
     dim3 grid((g->rows + 4 * kRowsPerWave - 1) / (4 * kRowsPerWave), g->batch);
     if (vec)
-      hipLaunchKernelGGL((momentum_rows_kernel<T, true>), grid, dim3(256), 0, s, (T*)M, (const T*)G,
-                         g->rows, g->cols, g->batch_stride, pkey, psq, pidx, pk, mu);
+      (void)launch((momentum_rows_kernel<T, true>), grid, dim3(256), s, (T*)M, (const T*)G, g->rows, g->cols, g->batch_stride, pkey, psq, pidx, pk, mu);
     else
-      hipLaunchKernelGGL((momentum_rows_kernel<T, false>), grid, dim3(256), 0, s, (T*)M, (const T*)G,
-                         g->rows, g->cols, g->batch_stride, pkey, psq, pidx, pk, mu);
+      (void)launch((momentum_rows_kernel<T, false>), grid, dim3(256), s, (T*)M, (const T*)G, g->rows, g->cols, g->batch_stride, pkey, psq, pidx, pk, mu);
   } else {
     const bool vec8 = vec && g->cols % 8 == 0;
     dim3 grid((g->cols + kColBlock - 1) / kColBlock, nchunks_for(1, g->rows), g->batch);
     if (vec8)
-      hipLaunchKernelGGL((momentum_cols_kernel<T, true>), grid, dim3(256), 0, s, (T*)M, (const T*)G,
-                         g->rows, g->cols, g->batch_stride, pkey, psq, pidx, pk, mu);
+      (void)launch((momentum_cols_kernel<T, true>), grid, dim3(256), s, (T*)M, (const T*)G, g->rows, g->cols, g->batch_stride, pkey, psq, pidx, pk, mu);
     else
-      hipLaunchKernelGGL((momentum_cols_kernel<T, false>), grid, dim3(256), 0, s, (T*)M, (const T*)G,
-                         g->rows, g->cols, g->batch_stride, pkey, psq, pidx, pk, mu);
+      (void)launch((momentum_cols_kernel<T, false>), grid, dim3(256), s, (T*)M, (const T*)G, g->rows, g->cols, g->batch_stride, pkey, psq, pidx, pk, mu);
   }
 }
 
@@ -423,8 +419,7 @@ extern "C" int dion3_momentum_rowsel_ef(const dion3_group* g, void* M, const voi
   if (st) return st;
   {
     TimedLaunch tl("topk_select", s);
-    hipLaunchKernelGGL(topk_kernel, dim3(g->batch), dim3(kTopkThreads), 0, s, pkey, psq, n, nch, k,
-                       idx, keys, sel_sqnorm);
+    (void)launch(topk_kernel, dim3(g->batch), dim3(kTopkThreads), s, pkey, psq, n, nch, k, idx, keys, sel_sqnorm);
   }
   return launch_status();
 }

@@ -313,15 +313,12 @@ static void launch_gather(const dion3_group* g, int axis, int n, int m, const vo
                      aligned16(X);
     dim3 grid((k + 3) / 4, g->batch);
     if (vec)
-      hipLaunchKernelGGL((gather_rows_kernel<TS, TX, true>), grid, dim3(256), 0, s, (const TS*)M,
-                         g->batch_stride, n, m, idx, k, sqn, eps, (TX*)X);
+      (void)launch((gather_rows_kernel<TS, TX, true>), grid, dim3(256), s, (const TS*)M, g->batch_stride, n, m, idx, k, sqn, eps, (TX*)X);
     else
-      hipLaunchKernelGGL((gather_rows_kernel<TS, TX, false>), grid, dim3(256), 0, s, (const TS*)M,
-                         g->batch_stride, n, m, idx, k, sqn, eps, (TX*)X);
+      (void)launch((gather_rows_kernel<TS, TX, false>), grid, dim3(256), s, (const TS*)M, g->batch_stride, n, m, idx, k, sqn, eps, (TX*)X);
   } else {
     dim3 grid((m + 63) / 64, (k + 63) / 64, g->batch);
-    hipLaunchKernelGGL((gather_cols_kernel<TS, TX>), grid, dim3(256), 0, s, (const TS*)M,
-                       g->batch_stride, g->rows, g->cols, idx, k, sqn, eps, (TX*)X);
+    (void)launch((gather_cols_kernel<TS, TX>), grid, dim3(256), s, (const TS*)M, g->batch_stride, g->rows, g->cols, idx, k, sqn, eps, (TX*)X);
   }
 }
 
@@ -335,24 +332,19 @@ static void launch_apply(const dion3_group* g, int axis, int n, int m, void* W, 
   TimedLaunch tl(W ? "apply_update" : "decay_rows", s);
   if (decay && W) {
     dim3 grid((g->rows + 7) / 8, g->batch);
-    hipLaunchKernelGGL((decay_unselected_kernel<TS>), grid, dim3(256), 0, s, (TS*)W, g->batch_stride,
-                       g->rows, g->cols, axis, n, idx, k, u);
+    (void)launch((decay_unselected_kernel<TS>), grid, dim3(256), s, (TS*)W, g->batch_stride, g->rows, g->cols, axis, n, idx, k, u);
   }
   if (axis == 0) {
     const bool vec = m % 8 == 0 && (g->batch == 1 || (g->batch_stride % 8 == 0 && ostride % 8 == 0)) &&
                      aligned16(W) && aligned16(M) && aligned16(O);
     dim3 grid((k + 3) / 4, g->batch);
     if (vec)
-      hipLaunchKernelGGL((apply_rows_kernel<TS, TO, true>), grid, dim3(256), 0, s, (TS*)W, (TS*)M,
-                         g->batch_stride, n, m, idx, k, (const TO*)O, ostride, rs, eta, u, decay, mu);
+      (void)launch((apply_rows_kernel<TS, TO, true>), grid, dim3(256), s, (TS*)W, (TS*)M, g->batch_stride, n, m, idx, k, (const TO*)O, ostride, rs, eta, u, decay, mu);
     else
-      hipLaunchKernelGGL((apply_rows_kernel<TS, TO, false>), grid, dim3(256), 0, s, (TS*)W, (TS*)M,
-                         g->batch_stride, n, m, idx, k, (const TO*)O, ostride, rs, eta, u, decay, mu);
+      (void)launch((apply_rows_kernel<TS, TO, false>), grid, dim3(256), s, (TS*)W, (TS*)M, g->batch_stride, n, m, idx, k, (const TO*)O, ostride, rs, eta, u, decay, mu);
   } else {
     dim3 grid((m + 63) / 64, (k + 63) / 64, g->batch);
-    hipLaunchKernelGGL((apply_cols_kernel<TS, TO>), grid, dim3(256), 0, s, (TS*)W, (TS*)M,
-                       g->batch_stride, g->rows, g->cols, idx, k, (const TO*)O, ostride, rs, eta, u,
-                       decay, mu);
+    (void)launch((apply_cols_kernel<TS, TO>), grid, dim3(256), s, (TS*)W, (TS*)M, g->batch_stride, g->rows, g->cols, idx, k, (const TO*)O, ostride, rs, eta, u, decay, mu);
   }
 }
 
@@ -363,14 +355,12 @@ int selected_sqnorm(const dion3_group* g, int axis, const void* M, const int32_t
   TimedLaunch tl("selected_norm", s);
   dim3 grid((k + 3) / 4, g->batch);
   if (g->dtype == DION3_BF16)
-    hipLaunchKernelGGL((line_sqsum_kernel<bf16_t>), grid, dim3(256), 0, s, (const bf16_t*)M, g->batch_stride,
-                       g->rows, g->cols, axis, idx, k, line_ws);
+    (void)launch((line_sqsum_kernel<bf16_t>), grid, dim3(256), s, (const bf16_t*)M, g->batch_stride, g->rows, g->cols, axis, idx, k, line_ws);
   else if (g->dtype == DION3_F32)
-    hipLaunchKernelGGL((line_sqsum_kernel<float>), grid, dim3(256), 0, s, (const float*)M, g->batch_stride,
-                       g->rows, g->cols, axis, idx, k, line_ws);
+    (void)launch((line_sqsum_kernel<float>), grid, dim3(256), s, (const float*)M, g->batch_stride, g->rows, g->cols, axis, idx, k, line_ws);
   else
     return DION3_ERR_INVALID_ARG;
-  hipLaunchKernelGGL(sum_lines_kernel, dim3(g->batch), dim3(256), 0, s, (const double*)line_ws, k, sqn);
+  (void)launch(sum_lines_kernel, dim3(g->batch), dim3(256), s, (const double*)line_ws, k, sqn);
   return launch_status();
 }
 

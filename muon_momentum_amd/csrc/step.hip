@@ -184,10 +184,12 @@ static int run_step(int n_groups, const dion3_group* groups, void* const* W, voi
   hipStream_t s = (hipStream_t)stream;
 
   // graph capture of the multi-stream step is not supported: refuse before
-  // anything is enqueued
-  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(s, &cap) != hipSuccess) return DION3_ERR_HIP;
-  if (cap != hipStreamCaptureStatusNone) return DION3_ERR_UNSUPPORTED;
+  // anything is enqueued (a step graph built node by node, graph.hip, is)
+  if (!graph_builder()) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cap) != hipSuccess) return DION3_ERR_HIP;
+    if (cap != hipStreamCaptureStatusNone) return DION3_ERR_UNSUPPORTED;
+  }
 
   std::lock_guard<std::mutex> lock(g_side_mu);
   SideCtx* ctx = nullptr;
@@ -200,7 +202,6 @@ static int run_step(int n_groups, const dion3_group* groups, void* const* W, voi
   hipEvent_t ev_fork = ev_upd[nc];              // first class selected (caller's stream)
   hipEvent_t ev_side_end = ev_upd[nc + 1];      // side stream drained
   hipEvent_t ev_mem_end = ev_upd[nc + 2];       // overlapped stream drained
-  auto hip_ok = [](hipError_t e) { return e == hipSuccess ? DION3_OK : DION3_ERR_HIP; };
   // class c's momentum + selection and gather: the caller's stream for the
   // first class, else the overlapped stream; class c's update: the caller's
   // stream for the last class, else the overlapped stream
@@ -224,7 +225,7 @@ static int run_step(int n_groups, const dion3_group* groups, void* const* W, voi
                                    deferred && has_prev ? idx[i] : nullptr, k[i], mu, rs_ws, P.rowsel, sc);
       if (r) return r;
     }
-    if (c >= 2 && (r = hip_ok(hipStreamWaitEvent(sc, ev_ns[c - 2], 0)))) return r;
+    if (c >= 2 && (r = stream_wait(sc, ev_ns[c - 2]))) return r;
     int nb = 0;
     for (int i : cls) {
       const dion3_group& gi = groups[i];
@@ -233,14 +234,14 @@ static int run_step(int n_groups, const dion3_group* groups, void* const* W, voi
       if (r) return r;
       nb += gi.batch;
     }
-    return hip_ok(hipEventRecord(ev_sel[c], sc));
+    return event_record(ev_sel[c], sc);
   };
 
   st = select_and_gather(0);
   if (!st && nc > 1) {
     // the overlapped stream starts once the first class is gathered
-    st = hip_ok(hipEventRecord(ev_fork, s));
-    if (!st) st = hip_ok(hipStreamWaitEvent(mem, ev_fork, 0));
+    st = event_record(ev_fork, s);
+    if (!st) st = stream_wait(mem, ev_fork);
     used_mem = used_mem || !st;
   }
   for (int c = 0; c < nc && !st; ++c) {
@@ -249,23 +250,23 @@ static int run_step(int n_groups, const dion3_group* groups, void* const* W, voi
     const size_t slice = (size_t)kk * mm * es;
     char* O = Obuf[c & 1];
     // Newton-Schulz of class c on the side stream
-    st = hip_ok(hipStreamWaitEvent(side, ev_sel[c], 0));
+    st = stream_wait(side, ev_sel[c]);
     used_side = used_side || !st;
     // O is rewritten two classes later: wait until that class's update read it
-    if (!st && c >= 2) st = hip_ok(hipStreamWaitEvent(side, ev_upd[c - 2], 0));
+    if (!st && c >= 2) st = stream_wait(side, ev_upd[c - 2]);
     int nb = 0;
     for (int i : cls) nb += groups[i].batch;
     // aspect ratio 1: standard Newton-Schulz on the symmetric kernels (fewer
     // launches, equal work); otherwise Gram Newton-Schulz
     if (!st) st = mm == kk ? dion3_standard_ns(nb, kk, mm, p, X0buf[c & 1], O, gws, P.gram, side)
                            : dion3_gram_ns_gathered(nb, kk, mm, p, X0buf[c & 1], O, gws, P.gram, side);
-    if (!st) st = hip_ok(hipEventRecord(ev_ns[c], side));
+    if (!st) st = event_record(ev_ns[c], side);
     // the next class's momentum and gather go ahead of this class's update
     // on the overlapped stream, so that they run beside these products
     if (!st && c + 1 < nc) st = select_and_gather(c + 1);
     // the update of class c
     hipStream_t uc = upd_stream(c);
-    if (!st) st = hip_ok(hipStreamWaitEvent(uc, ev_ns[c], 0));
+    if (!st) st = stream_wait(uc, ev_ns[c]);
     nb = 0;
     for (int i : cls) {
       if (st) break;
@@ -279,13 +280,13 @@ static int run_step(int n_groups, const dion3_group* groups, void* const* W, voi
                                      p->ns_dtype, (long long)kk * mm, rsc, eta, wd, mu, uc);
       nb += gi.batch;
     }
-    if (!st) st = hip_ok(hipEventRecord(ev_upd[c], uc));
+    if (!st) st = event_record(ev_upd[c], uc);
   }
   // join: the caller's stream waits for everything enqueued on the library
   // streams (also after an error, so that no such work escapes the call's order)
   auto join = [&](hipStream_t from, hipEvent_t e) {
-    const int j = hip_ok(hipEventRecord(e, from));
-    const int w = j ? j : hip_ok(hipStreamWaitEvent(s, e, 0));
+    const int j = event_record(e, from);
+    const int w = j ? j : stream_wait(s, e);
     if (!st) st = w;
   };
   if (used_side) join(side, ev_side_end);
@@ -308,6 +309,16 @@ extern "C" int dion3_step_deferred(int n_groups, const dion3_group* groups, void
   return run_step(n_groups, groups, W, M, G, k, idx, p, eta, wd, mu, ws, ws_bytes, stream, true,
                   has_prev != 0);
 }
+
+namespace dion3 {
+int run_step_deferred(int n_groups, const dion3_group* groups, void* const* W, void* const* M,
+                      const void* const* G, const int* k, int32_t* const* idx, int has_prev,
+                      const dion3_ns_params* p, float eta, float wd, float mu, void* ws, size_t ws_bytes,
+                      void* stream) {
+  return run_step(n_groups, groups, W, M, G, k, idx, p, eta, wd, mu, ws, ws_bytes, stream, true,
+                  has_prev != 0);
+}
+}  // namespace dion3
 
 extern "C" int dion3_step_normuon(int n_groups, const dion3_group* groups, void* const* W,
                                   void* const* M, const void* const* G, const int* k,

@@ -88,6 +88,11 @@ def _load() -> ctypes.CDLL:
         "dion3_step_workspace_bytes": (sz, [i, gp, ctypes.POINTER(i), pp]),
         "dion3_step": (i, [i, gp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
                            ctypes.POINTER(i), ctypes.POINTER(vp), pp, f, f, f, vp, sz, vp]),
+        "dion3_step_graph_create": (i, [i, gp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                        ctypes.POINTER(i), ctypes.POINTER(vp), i, pp, f, f, f, vp, sz,
+                                        ctypes.POINTER(vp)]),
+        "dion3_graph_launch": (i, [vp, vp]),
+        "dion3_graph_destroy": (i, [vp]),
         "dion3_timing_enable": (i, [i]),
         "dion3_timing_report": (i, [ctypes.c_char_p, sz]),
     }
@@ -353,12 +358,45 @@ class StepPlan:
                                       eta, wd, mu, beta2, nm_eps, _ptr(self.ws), self.ws.numel(),
                                       _stream()), "dion3_step_normuon")
 
+    def graph(self, eta, wd, mu, has_prev=True):
+        """dion3_step_graph_create: the deferred step as an instantiated HIP
+        graph over this plan's tensors and workspace (StepGraph)."""
+        g = ctypes.c_void_p()
+        _check(lib.dion3_step_graph_create(self.n, self.groups, self.W, self.M, self.G, self.k, self.idx,
+                                           1 if has_prev else 0, ctypes.byref(self.params), eta, wd, mu,
+                                           _ptr(self.ws), self.ws.numel(), ctypes.byref(g)),
+               "dion3_step_graph_create")
+        return StepGraph(g, self)
+
     def flush_decay(self, mu):
         """Complete the pending decay of the last deferred step on every group."""
         Ws, Ms, Gs, idxs = self._keep
         for M, idx, k, g in zip(Ms, idxs, self.k, self.groups):
             _check(lib.dion3_decay_rows(ctypes.byref(g), _ptr(M), _ptr(idx), k, mu, _stream()),
                    "dion3_decay_rows")
+
+
+class StepGraph:
+    """An instantiated step graph; launch() enqueues one step on the current
+    stream.  Holds its plan (tensors and workspace) alive."""
+
+    def __init__(self, handle, plan):
+        self._h = handle
+        self._plan = plan
+
+    def launch(self):
+        _check(lib.dion3_graph_launch(self._h, _stream()), "dion3_graph_launch")
+
+    def destroy(self):
+        if self._h:
+            _check(lib.dion3_graph_destroy(self._h), "dion3_graph_destroy")
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
 
 
 def dion3_step(Ws, Ms, Gs, ks, idxs, eta, wd, mu, params=None, sel_axes=None):

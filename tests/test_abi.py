@@ -225,3 +225,28 @@ def test_release_without_gpu_work_is_a_no_op():
     it makes no HIP call and succeeds (twice in a row as well)."""
     assert d.lib.dion3_release() == 0
     assert d.lib.dion3_release() == 0
+
+
+def test_step_graph_argument_checks():
+    """dion3_step_graph_create validates like the step before any HIP call;
+    launching or destroying a missing graph is handled."""
+    L = d.lib
+    p = d.make_ns_params()
+    pp = ctypes.byref(p)
+    groups = (d.Group * 2)(d.Group(64, 128, 2, 64 * 128, d.BF16, -1), d.Group(128, 64, 1, 128 * 64, d.BF16, -1))
+    ks = (ctypes.c_int * 2)(16, 16)
+    ptrs = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    sw = L.dion3_step_workspace_bytes(2, groups, ks, pp)
+    out = ctypes.c_void_p()
+    args = (ptrs, ptrs, ptrs, ks, ptrs, 1, pp, 0.1, 0.0, 0.9)
+    assert L.dion3_step_graph_create(2, groups, *args, FAKE, sw - 1, ctypes.byref(out)) == -3
+    assert L.dion3_step_graph_create(2, groups, *args, FAKE, sw, None) == -1
+    bad = (ctypes.c_int * 2)(16, 65)
+    assert L.dion3_step_graph_create(2, groups, ptrs, ptrs, ptrs, bad, ptrs, 1, pp, 0.1, 0.0, 0.9, FAKE, sw,
+                                     ctypes.byref(out)) == -1
+    nulls = (ctypes.c_void_p * 2)(0x1000, None)
+    assert L.dion3_step_graph_create(2, groups, nulls, ptrs, ptrs, ks, ptrs, 1, pp, 0.1, 0.0, 0.9, FAKE, sw,
+                                     ctypes.byref(out)) == -1
+    assert out.value is None
+    assert L.dion3_graph_launch(None, None) == -1
+    assert L.dion3_graph_destroy(None) == 0

@@ -1,0 +1,80 @@
+"""The deferred step as a HIP graph built node by node (no stream capture;
+"Dion3: Full-Stack Orthogonal Updates", Section 6: the step's launches have
+the same dependencies every step, so one graph is replayed per step).
+
+A graph is created once over one set of tensors and replayed several times;
+between replays new gradients are copied in and the same step runs eagerly on
+a copy, with synchronisations around every replay.  After every replay the
+selected indices, W and M (which both owe the same pending decay) must equal
+the eager step's bit for bit."""
+
+import math
+
+import pytest
+import torch
+
+from muon_momentum_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def d():
+    import muon_momentum_amd.dion3 as mod
+    return mod
+
+
+def _state(shapes, ks, seed0=0):
+    Ws, Ms, Gs, ids = [], [], [], []
+    for gi, (r, c, b) in enumerate(shapes):
+        Ws.append(synth.weights(r, c, b, dtype="bf16", device=DEV, group_seed=seed0 + gi))
+        Gs.append(synth.gradient(r, c, b, dtype="bf16", device=DEV, group_seed=seed0 + gi, step=0))
+        Ms.append(torch.zeros(b, r, c, dtype=Ws[-1].dtype, device=DEV))
+        ids.append(torch.empty(b, ks[gi], dtype=torch.int32, device=DEV))
+    return Ws, Ms, Gs, ids
+
+
+def _replays_match(d, shapes, f, replays, seed0=0):
+    ks = [d.dion3_k_from_fraction(min(r, c), f) for r, c, _ in shapes]
+    mu, eta = 0.95, 0.02 / math.sqrt(f)
+    params = d.make_ns_params(ns_dtype=d.F16)
+    A = _state(shapes, ks, seed0)
+    B = [[t.clone() for t in ts] for ts in A]
+    pa = d.StepPlan(A[0], A[1], A[2], ks, A[3], params)
+    pb = d.StepPlan(B[0], B[1], B[2], ks, B[3], params)
+    pa.step_deferred(eta, 0.0, mu, has_prev=False)
+    pb.step_deferred(eta, 0.0, mu, has_prev=False)
+    torch.cuda.synchronize()
+    graph = pb.graph(eta, 0.0, mu, has_prev=True)
+    torch.cuda.synchronize()
+    for step in range(1, replays + 1):
+        for gi, (r, c, b) in enumerate(shapes):
+            Gn = synth.gradient(r, c, b, dtype="bf16", device=DEV, group_seed=seed0 + gi, step=step)
+            A[2][gi].copy_(Gn)
+            B[2][gi].copy_(Gn)
+            del Gn
+        torch.cuda.synchronize()
+        pa.step_deferred(eta, 0.0, mu, has_prev=True)
+        torch.cuda.synchronize()
+        graph.launch()
+        torch.cuda.synchronize()
+        for gi in range(len(shapes)):
+            assert torch.equal(A[3][gi], B[3][gi]), ("idx", step, gi)
+            assert torch.equal(A[0][gi].view(torch.int16), B[0][gi].view(torch.int16)), ("W", step, gi)
+            assert torch.equal(A[1][gi].view(torch.int16), B[1][gi].view(torch.int16)), ("M", step, gi)
+    graph.destroy()
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("f", [0.25, 1.0])
+def test_step_graph_replays_match_eager(d, f):
+    # three (k, m) classes (rows and columns selected together), a square class
+    # at f = 1, and 256 x 256 tiles (the 1024-row groups)
+    _replays_match(d, [(256, 1024, 6), (1024, 256, 3), (512, 512, 2), (1024, 2048, 2)], f, replays=4)
+
+
+@pytest.mark.timeout(600)
+def test_step_graph_7b_matches_eager(d):
+    """The benchmarked workload: 7B shape set, f = 1/4, two replays."""
+    _replays_match(d, synth.shape_groups("7b"), 0.25, replays=2, seed0=0)
