@@ -188,6 +188,7 @@ struct GemmArgs {
   const void* E; long long lde, sE;     // epilogue operand (beta term), may be null
   void* C; long long ldc, sC;
   float alpha, beta, gamma;
+  int reverse = 0;    // visit the batch from its last matrix (tile order only)
 };
 
 int launch_gemm(const GemmArgs& a, hipStream_t s);

@@ -81,6 +81,7 @@ struct KParams {
   int tiles_m, tiles_n, tiles_per_mat;
   int ntiles;          // tiles over the batch
   int tiles_per_wg;    // large-tile kernel: tiles run back to back by one work-group
+  int reverse;         // batch visited from its last matrix
 };
 
 // LDS position of 16-byte chunk `chunk` of tile row `row`.  A 128-bit LDS read
@@ -155,8 +156,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(KParams p) {
   const int wg = blockIdx.x;
   const int per = G / 8;
   const int id = wg < per * 8 ? (wg % 8) * per + wg / 8 : wg;
-  const int bat = id / p.tiles_per_mat;
   const int t = id % p.tiles_per_mat;
+  const int bat = p.reverse ? p.ntiles / p.tiles_per_mat - 1 - id / p.tiles_per_mat : id / p.tiles_per_mat;
   int ti, tj;
   if (SYM) {
     tri_index(t, ti, tj);
@@ -527,6 +528,7 @@ void gemm256_kernel(KParams p) {
   auto tile_addr = [&](int L, TileAddr& a) {
     int bat = L / p.tiles_per_mat;
     const int t = L - bat * p.tiles_per_mat;
+    if (p.reverse) bat = p.ntiles / p.tiles_per_mat - 1 - bat;
     int ti, tj;
     if (SYM) {
       tri_index(t, ti, tj);
@@ -1128,6 +1130,7 @@ static int launch_typed(const GemmArgs& a, hipStream_t s) {
   p.E = a.E; p.lde = a.lde; p.sE = a.sE;
   p.C = a.C; p.ldc = a.ldc; p.sC = a.sC;
   p.alpha = a.alpha; p.beta = a.beta; p.gamma = a.gamma;
+  p.reverse = a.reverse;
 
   // The 256 x 256 tile is used for fp16 / bf16 when the shape is a whole
   // number of tiles and there are at least 128 of them (half the compute

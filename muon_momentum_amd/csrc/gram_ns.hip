@@ -24,8 +24,9 @@ static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 static int sym_op(int op, int batch, int n, int K, int dtype, const void* A, long long sA,
                   const void* B, long long sB, const void* E, long long sE, void* C, long long sC,
-                  float alpha, float beta, float gamma, hipStream_t s) {
+                  float alpha, float beta, float gamma, hipStream_t s, bool rev = false) {
   GemmArgs g;
+  g.reverse = rev;
   g.op = op; g.dtype = dtype; g.out_dtype = dtype; g.batch = batch;
   g.M = n; g.N = n; g.K = K;
   g.A = A; g.lda = K; g.sA = sA;
@@ -37,8 +38,10 @@ static int sym_op(int op, int batch, int n, int K, int dtype, const void* A, lon
 }
 
 static int qx_op(int batch, int k, int m, int in_dtype, const void* Q, long long sQ, const void* X,
-                 long long sX, int out_dtype, void* Y, long long sY, float alpha, hipStream_t s) {
+                 long long sX, int out_dtype, void* Y, long long sY, float alpha, hipStream_t s,
+                 bool rev = false) {
   GemmArgs g;
+  g.reverse = rev;
   g.op = OP_GEMM; g.dtype = in_dtype; g.out_dtype = out_dtype; g.batch = batch;
   g.M = k; g.N = m; g.K = k;
   g.A = Q; g.lda = k; g.sA = sQ;
@@ -140,27 +143,36 @@ extern "C" int dion3_gram_ns_gathered(int batch, int k, int m, const dion3_ns_pa
   };
   auto give = [&](int i) { if (i >= 0) used[i] = false; };
 
+  // Consecutive products visit the batch in opposite orders, so each starts on
+  // the matrices the previous one finished last, whose operands the
+  // last-level cache may still hold (the first starts at the end the gather
+  // wrote last).
+  bool rev = true;
+  auto order = [&]() { const bool r = rev; rev = !rev; return r; };
+
   const void* cur = X0;
   int st = DION3_OK;
   for (int ps = 0; ps < npass && st == DION3_OK; ++ps) {
     const int t0 = bounds[ps], t1 = bounds[ps + 1];
     void* out = ((npass - 1 - ps) % 2 == 0) ? O : X2;
     const int R = take();
-    st = sym_op(OP_SYRK, batch, k, m, dt, cur, skm, cur, skm, nullptr, 0, sq[R], skk, 1.f, 0.f, 0.f, s);
+    st = sym_op(OP_SYRK, batch, k, m, dt, cur, skm, cur, skm, nullptr, 0, sq[R], skk, 1.f, 0.f, 0.f, s,
+                order());
     int Q = -1;
     for (int t = t0; t < t1 && st == DION3_OK; ++t) {
       const float a = (float)p->coeffs[3 * t + 0];
       const float b = (float)p->coeffs[3 * t + 1];
       const float c = (float)p->coeffs[3 * t + 2];
       const int Z = take();
-      st = sym_op(OP_SQ_ADD, batch, k, k, dt, sq[R], skk, sq[R], skk, sq[R], skk, sq[Z], skk, c, b, a, s);
+      st = sym_op(OP_SQ_ADD, batch, k, k, dt, sq[R], skk, sq[R], skk, sq[R], skk, sq[Z], skk, c, b, a, s,
+                  order());
       if (st) break;
       if (Q < 0) {
         Q = Z;
       } else {
         const int Qn = take();
         st = sym_op(OP_SYM_MUL, batch, k, k, dt, sq[Q], skk, sq[Z], skk, nullptr, 0, sq[Qn], skk, 1.f, 0.f,
-                    0.f, s);
+                    0.f, s, order());
         give(Q);
         Q = Qn;
         if (st) break;
@@ -168,16 +180,16 @@ extern "C" int dion3_gram_ns_gathered(int batch, int k, int m, const dion3_ns_pa
       if (t < t1 - 1) {
         const int P = take();
         st = sym_op(OP_SYM_MUL, batch, k, k, dt, sq[Z], skk, sq[R], skk, nullptr, 0, sq[P], skk, 1.f, 0.f,
-                    0.f, s);
+                    0.f, s, order());
         if (!st)
           st = sym_op(OP_SYM_MUL, batch, k, k, dt, sq[P], skk, sq[Z], skk, nullptr, 0, sq[R], skk, 1.f, 0.f,
-                      0.f, s);
+                      0.f, s, order());
         give(P);
       }
       if (Z != Q) give(Z);
     }
     if (st) break;
-    st = qx_op(batch, k, m, dt, sq[Q], skk, cur, skm, dt, out, skm, 1.f, s);
+    st = qx_op(batch, k, m, dt, sq[Q], skk, cur, skm, dt, out, skm, 1.f, s, order());
     give(Q);
     give(R);
     cur = out;
@@ -268,6 +280,8 @@ extern "C" int dion3_standard_ns(int batch, int k, int m, const dion3_ns_params*
   void* Xw = w;
   void* A = w + align256((size_t)batch * skm * es);
   void* Z = (char*)A + align256((size_t)batch * skk * es);
+  bool rev = true;     // alternate batch orders, as in the Gram form
+  auto order = [&]() { const bool r = rev; rev = !rev; return r; };
   const void* cur = X0;
   int st = DION3_OK;
   for (int t = 0; t < p->T && st == DION3_OK; ++t) {
@@ -275,9 +289,9 @@ extern "C" int dion3_standard_ns(int batch, int k, int m, const dion3_ns_params*
     const float b = (float)p->coeffs[3 * t + 1];
     const float c = (float)p->coeffs[3 * t + 2];
     void* out = ((p->T - 1 - t) % 2 == 0) ? O : Xw;
-    st = sym_op(OP_SYRK, batch, k, m, dt, cur, skm, cur, skm, nullptr, 0, A, skk, 1.f, 0.f, 0.f, s);
-    if (!st) st = sym_op(OP_SQ_ADD, batch, k, k, dt, A, skk, A, skk, A, skk, Z, skk, c, b, a, s);
-    if (!st) st = qx_op(batch, k, m, dt, Z, skk, cur, skm, dt, out, skm, 1.f, s);
+    st = sym_op(OP_SYRK, batch, k, m, dt, cur, skm, cur, skm, nullptr, 0, A, skk, 1.f, 0.f, 0.f, s, order());
+    if (!st) st = sym_op(OP_SQ_ADD, batch, k, k, dt, A, skk, A, skk, A, skk, Z, skk, c, b, a, s, order());
+    if (!st) st = qx_op(batch, k, m, dt, Z, skk, cur, skm, dt, out, skm, 1.f, s, order());
     cur = out;
   }
   return st;
