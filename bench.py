@@ -125,30 +125,45 @@ def measured_traffic(kernel: str, set_name: str, f: float):
 
 
 # ------------------------------------------------------------ work accounting
-def kernel_work(groups, ks, ns_bytes=2, store_bytes=2):
+def fuses_update(rows, cols, b, k, flavor):
+    """Whether the deferred Muon step updates this bf16 group inside its last
+    Q X product (row-selected, whole 256 x 256 tiles, at least 128 of them)."""
+    m = max(rows, cols)
+    return (flavor == "muon" and rows <= cols and k % 256 == 0 and m % 256 == 0
+            and b * (k // 256) * (m // 256) >= 128)
+
+
+def kernel_work(groups, ks, ns_bytes=2, store_bytes=2, flavor="muon"):
     """Algorithmic work per step of every kernel class of the library.
 
     Bytes: momentum_keys reads M, G and writes M (3 x storage bytes per
     parameter; the deferred decay of the previous selection rides along);
     gather_scale reads each selected element and writes it in the
     Newton-Schulz type; apply_update reads and writes W and reads O per
-    selected element (the decay of M is deferred to the next momentum pass).  FLOPs: a symmetric product counts only its lower
-    triangle (k(k+1)/2 entries, 2 x contraction length each); Q X is a full
-    k x k by k x m product.  Returns {name: (kind, units per step)}."""
+    selected element (the decay of M is deferred to the next momentum pass).
+    FLOPs: a symmetric product counts only its lower triangle (k(k+1)/2
+    entries, 2 x contraction length each); Q X is a full k x k by k x m
+    product; qx_apply is the last Q X of a group whose update it fuses (that
+    group then has no apply_update).  Returns {name: (kind, units per step)}."""
     w = {"momentum_keys": 0.0, "topk_select": 0.0, "gather_scale": 0.0, "apply_update": 0.0,
-         "syrk": 0.0, "sym_sq_add": 0.0, "sym_mul": 0.0, "gemm_qx": 0.0, "normuon_scale": 0.0}
+         "syrk": 0.0, "sym_sq_add": 0.0, "sym_mul": 0.0, "gemm_qx": 0.0, "qx_apply": 0.0,
+         "normuon_scale": 0.0}
     for (rows, cols, b), k in zip(groups, ks):
         n, m = min(rows, cols), max(rows, cols)
+        fused = fuses_update(rows, cols, b, k, flavor)
         w["momentum_keys"] += b * rows * cols * 3 * store_bytes
         w["topk_select"] += b * n * 8 * 2
         w["gather_scale"] += b * k * m * (store_bytes + ns_bytes)
-        w["apply_update"] += b * k * m * (2 * store_bytes + ns_bytes)
+        if not fused:
+            w["apply_update"] += b * k * m * (2 * store_bytes + ns_bytes)
         tri = k * (k + 1) / 2
+        last_qx = "qx_apply" if fused else "gemm_qx"
         if k == m:
             # square class: standard Newton-Schulz, per iteration X X^T, A^2 + B, Z X
             w["syrk"] += b * 5 * tri * 2 * m
             w["sym_sq_add"] += b * 5 * tri * 2 * k
-            w["gemm_qx"] += b * 5 * 2 * k * k * m
+            w["gemm_qx"] += b * 4 * 2 * k * k * m
+            w[last_qx] += b * 2 * k * k * m
         else:
             passes, iters = 2, 5                     # restart after iteration 2
             w["syrk"] += b * passes * tri * 2 * m
@@ -156,12 +171,13 @@ def kernel_work(groups, ks, ns_bytes=2, store_bytes=2):
             # Q products: one per iteration except a pass's first (3); Z R Z: two
             # products per iteration except a pass's last (3 iterations -> 6)
             w["sym_mul"] += b * (3 + 6) * tri * 2 * k
-            w["gemm_qx"] += b * passes * 2 * k * k * m
+            w["gemm_qx"] += b * (passes - 1) * 2 * k * k * m
+            w[last_qx] += b * 2 * k * k * m
         # NorMuon flavour: read O once, then the moments and factors
         w["normuon_scale"] += b * k * (m * ns_bytes + 4 * 4)
     kind = {"momentum_keys": "hbm", "topk_select": "hbm", "gather_scale": "hbm",
             "apply_update": "hbm", "syrk": "mfma", "sym_sq_add": "mfma", "sym_mul": "mfma",
-            "gemm_qx": "mfma", "normuon_scale": "hbm"}
+            "gemm_qx": "mfma", "qx_apply": "mfma", "normuon_scale": "hbm"}
     return {name: (kind[name], v) for name, v in w.items()}
 
 
@@ -304,7 +320,7 @@ def run_step_bench(d, synth, torch, args):
     d.dion3_timing_enable(0)
     print(f"# instrumented {nprof} steps: {pct['instrumented']:.3f} ms/step", file=sys.stderr, flush=True)
 
-    work = kernel_work(groups, ks)
+    work = kernel_work(groups, ks, flavor=args.flavor)
     table = {}
     for name, (cnt, total_ms) in per_kernel.items():
         kind, units = work.get(name, ("?", 0.0))

@@ -315,7 +315,10 @@ int dion3_step(int n_groups, const dion3_group* groups, void* const* W, void* co
  * has_prev != 0 (it is decayed, then overwritten by this step's selection);
  * pass has_prev = 0 on the first step.  After a call, M[i] still owes the
  * decay of the lines in idx[i]: dion3_decay_rows completes it.  The sequence
- * of W, M (once completed) and idx is bit-identical to dion3_step's. */
+ * of W, M (once completed) and idx is bit-identical to dion3_step's.  Since
+ * the update then leaves M alone, the last Newton-Schulz product of a
+ * row-selected bf16 group (whole 256 x 256 tiles) updates W itself instead
+ * of writing O, with the same arithmetic as dion3_apply_rows. */
 int dion3_step_deferred(int n_groups, const dion3_group* groups, void* const* W, void* const* M,
                         const void* const* G, const int* k, int32_t* const* idx, int has_prev,
                         const dion3_ns_params* p, float eta, float wd, float mu,

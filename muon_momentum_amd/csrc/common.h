@@ -26,13 +26,18 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
 
-// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.  Written as a
-// select so that it does not branch inside a wave.
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-  const uint32_t quiet = (u >> 16) | 0x40u;
-  return (bf16_t)(((u & 0x7fffffffu) > 0x7f800000u) ? quiet : rounded);
+// fp32 -> bf16, round to nearest even; a NaN keeps its sign and upper payload
+// bits with the quiet bit set, i.e. for bit pattern u: (u >> 16) | 0x40 if u
+// is a NaN, else (u + 0x7fff + ((u >> 16) & 1)) >> 16.  gfx950's
+// v_cvt_pk_bf16_f32 computes exactly this (compared on all 2^32 inputs, in
+// the default floating-point mode these kernels run in); the pair form
+// converts two values with one instruction.
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
+typedef float f32x2_hw __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+  const f32x2_hw v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_hw));
 }
 
 // fp64 -> bf16 with a single round-to-nearest-even of the fp64 value.
@@ -86,6 +91,17 @@ template <> __device__ __forceinline__ bf16_t decay_round<bf16_t>(float mu, bf16
   return f64_to_bf16((double)mu * (double)bf16_to_f32(m));
 }
 template <> __device__ __forceinline__ float decay_round<float>(float mu, float m) { return mu * m; }
+
+// The fused update of one selected entry of W: w' = round(fp32(a - eta o))
+// with a = fp32(u w) when decaying, else w ("Dion3: Full-Stack Orthogonal
+// Updates", Section 6: evaluated in fp32, cast back to storage once).  The
+// apply pass and the Q X epilogue that fuses it share this definition.
+template <typename T>
+__device__ __forceinline__ T update_w(T w, float o, float eta, float u, bool decay) {
+  float a = Store<T>::to_f32(w);
+  if (decay) a = u * a;
+  return Store<T>::from_f32(__builtin_fmaf(-eta, o, a));
+}
 
 // ------------------------------------------------------------- reductions
 __device__ __forceinline__ double wave_sum(double v) {
@@ -167,6 +183,31 @@ int run_step_deferred(int n_groups, const dion3_group* groups, void* const* W, v
                       const dion3_ns_params* p, float eta, float wd, float mu, void* ws, size_t ws_bytes,
                       void* stream);
 int event_record(hipEvent_t e, hipStream_t s);
+
+// u = fp32(1 - eta wd): the product is exact in fp64, one rounding to fp32
+inline float weight_decay_factor(float eta, float wd) { return (float)(1.0 - (double)eta * (double)wd); }
+
+// The last product of a Newton-Schulz call (O = Q X) with the update of W
+// fused into it for some groups of the batch: segment s covers matrices
+// [b0, b0 + nb) of the batch, those of one group; `fuse` asks for the fused
+// update of that group's W (bf16, rows selected by idx).  The call reports
+// per segment whether it fused (else it wrote that segment's O).
+struct FusedSegment {
+  int b0, nb;
+  void* W; long long sW; int wlines; const int32_t* idx;
+  bool fuse, fused;
+};
+struct FusedUpdate {
+  int nseg;
+  FusedSegment* seg;
+  float eta, u; int decay;
+};
+int gram_ns_gathered_fused(int batch, int k, int m, const dion3_ns_params* p, const void* X0, void* O, void* ws,
+                           size_t ws_bytes, void* stream, FusedUpdate* fu);
+int standard_ns_fused(int batch, int k, int m, const dion3_ns_params* p, const void* X0, void* O, void* ws,
+                      size_t ws_bytes, void* stream, FusedUpdate* fu);
+// Weight decay of the lines a step did not select (scatter.hip; W bf16 or fp32).
+int decay_unselected(const dion3_group* g, void* W, const int32_t* idx, int k, float u, hipStream_t s);
 int stream_wait(hipStream_t s, hipEvent_t e);
 
 // ||M[S,:]||_F^2 of every matrix of a group (scatter.hip); line_ws holds
@@ -189,8 +230,17 @@ struct GemmArgs {
   void* C; long long ldc, sC;
   float alpha, beta, gamma;
   int reverse = 0;    // visit the batch from its last matrix (tile order only)
+  // Q X with the update of W fused into the epilogue (OP_GEMM, large tiles,
+  // bf16 W): row r of matrix b's result, rounded to out_dtype, updates row
+  // idx[b][r] of W's matrix b (wlines rows of N elements, matrix stride sW)
+  // with update_w; C receives only the rows whose index is out of range.
+  void* W = nullptr; long long sW = 0; int wlines = 0; const int32_t* idx = nullptr;
+  float eta = 0.f, u = 1.f; int decay = 0;
 };
 
 int launch_gemm(const GemmArgs& a, hipStream_t s);
+// Whether launch_gemm runs `a` on the large-tile kernel (the only one that
+// can fuse the update).
+bool gemm_large_tile(const GemmArgs& a);
 
 }  // namespace dion3

@@ -82,6 +82,9 @@ struct KParams {
   int ntiles;          // tiles over the batch
   int tiles_per_wg;    // large-tile kernel: tiles run back to back by one work-group
   int reverse;         // batch visited from its last matrix
+  // fused update (large-tile Q X with APPLY): see GemmArgs
+  void* W; long long sW; int wlines; const int32_t* idx;
+  float eta, u; int decay;
 };
 
 // LDS position of 16-byte chunk `chunk` of tile row `row`.  A 128-bit LDS read
@@ -463,6 +466,39 @@ struct TileAddr {
 
 constexpr int kEpiStores = 32;   // 16-byte stores per wave in a Q X tile epilogue
 
+// 16-byte accesses of W rows in the fused update (each byte touched once)
+__device__ __forceinline__ uint4 ld_nt16(const void* p) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  const v4u x = __builtin_nontemporal_load((const v4u*)p);
+  return make_uint4(x.x, x.y, x.z, x.w);
+}
+__device__ __forceinline__ void st_nt16(void* p, const uint4& v) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  const v4u x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, (v4u*)p);
+}
+
+// update_w on 8 consecutive entries: W chunk w (bf16) with the rounded
+// results o (8 values of type TO) of the same columns
+// (update_w's arithmetic; the two results of a pair rounded by one
+// instruction, bit-identical to rounding each)
+template <typename TO>
+__device__ __forceinline__ uint4 update8(const uint4& w, const uint4& o, float eta, float u, bool decay) {
+  union { uint4 v; bf16_t e[8]; } wu;
+  union { uint4 v; TO e[8]; } ou;
+  union { uint4 v; uint32_t d[4]; } r;
+  wu.v = w;
+  ou.v = o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float a0 = bf16_to_f32(wu.e[2 * q]), a1 = bf16_to_f32(wu.e[2 * q + 1]);
+    if (decay) { a0 = u * a0; a1 = u * a1; }
+    r.d[q] = f32x2_to_bf16x2(__builtin_fmaf(-eta, Store<TO>::to_f32(ou.e[2 * q]), a0),
+                             __builtin_fmaf(-eta, Store<TO>::to_f32(ou.e[2 * q + 1]), a1));
+  }
+  return r.v;
+}
+
 typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v* lds_s4_ptr;
 
@@ -479,9 +515,17 @@ __device__ __forceinline__ uint4 lds_read16(unsigned addr) {
 // g - 2; the first k-step's fragments of stage g are then read during stage
 // g - 1, so a wave leaves every barrier with its next MFMA operands in
 // registers.  Each wave issues 8 one-kilobyte DMA instructions per stage.
-template <typename T, typename TO, int OP, int NBUF>
+//
+// APPLY (Q X only): the epilogue does not store the tile; each 16-byte chunk
+// of it (rounded to TO exactly as stored) updates the same columns of W row
+// idx[b][r] instead, the chunks of W loaded together at the start of the
+// epilogue.  Every store instruction is still issued (a row whose index is
+// out of range stores its chunk to C), so the count of stores in flight that
+// the next tile's waits allow for is the same.
+template <typename T, typename TO, int OP, int NBUF, bool APPLY = false>
 __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm256_kernel(KParams p) {
+  static_assert(!APPLY || (OP == OP_GEMM && sizeof(TO) == 2), "the update is fused into Q X only");
   constexpr bool SYM = OP != OP_GEMM;
   constexpr bool BT = OP == OP_GEMM;
   constexpr bool SWAP = true;                       // MFMA produces C^T blocks
@@ -595,10 +639,28 @@ void gemm256_kernel(KParams p) {
   // the next tile
   floatx16 acc[SUB][SUB];
 
+  // APPLY: the W row index of each output row this lane stores (rows
+  // m0 + 128 wm + (lane mod 8) + 32 i + 16 hh + 8 e of the tile), for the
+  // current tile and, loaded during its epilogue, the next one
+  int wr[SUB][2][2], wr_next[SUB][2][2];
+  auto load_rows = [&](const TileAddr& a, int (&dst)[SUB][2][2]) {
+    const int32_t* ib = p.idx + (long long)a.bat * p.M + a.m0 + wm * WT + (lane & 7);
+    static_for<SUB>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      static_for<2>([&](auto hc) {
+        constexpr int hh = decltype(hc)::value;
+        static_for<2>([&](auto ec) {
+          constexpr int e = decltype(ec)::value;
+          dst[i][hh][e] = ib[32 * i + 16 * hh + 8 * e];
+        });
+      });
+    });
+  };
+
   // Q X epilogue: block (i, j) of the wave holds C[row lane%32][8 g + 4 (lane/32)
   // + 0..3] in acc[i][j][4 g .. 4 g + 3]; a lane swap across the half-waves gives
   // lane L < 32 columns 16 h .. +7 and lane L + 32 columns 16 h + 8 .. +15
-  auto epilogue_swap = [&](const TileAddr& a) {
+  auto epilogue_swap = [&](const TileAddr& a, const TileAddr& an, bool more) {
     if constexpr (SWAP) {
       TO* C = (TO*)p.C + a.bat * p.sC;
       const int lc = lane & 31, lh = lane >> 5;
@@ -612,6 +674,35 @@ void gemm256_kernel(KParams p) {
       const int hi8 = (lc >> 3) & 1;
       TO* rowo = C + (long long)(a.m0 + wm * WT + (lc & 7)) * p.ldc + (a.n0 + wn * WT) + 32 * hi8 +
                  16 * ((lc >> 4) & 1) + 8 * lh;
+      // APPLY: the next tile's row indices, then the W chunks these stores
+      // update (row wr[i][hh][e], columns cw + 64 jj .. + 7), all loaded
+      // before the first is needed (the waits for the chunks, in issue order,
+      // also complete the indices)
+      bf16_t* Wb = nullptr;
+      int cw = 0;
+      uint4 wv[SUB][2][2][2];
+      if constexpr (APPLY) {
+        if (more) load_rows(an, wr_next);
+        Wb = (bf16_t*)p.W + a.bat * p.sW;
+        cw = a.n0 + wn * WT + 32 * hi8 + 16 * ((lc >> 4) & 1) + 8 * lh;
+        static_for<SUB>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          static_for<2>([&](auto hc) {
+            constexpr int hh = decltype(hc)::value;
+            static_for<2>([&](auto ec) {
+              constexpr int e = decltype(ec)::value;
+              // an out-of-range row loads row 0 (unused): every load is issued,
+              // so the waits for them can be counted
+              const int r = (unsigned)wr[i][hh][e] < (unsigned)p.wlines ? wr[i][hh][e] : 0;
+              static_for<2>([&](auto jc) {
+                constexpr int jj = decltype(jc)::value;
+                wv[i][hh][e][jj] = ld_nt16(Wb + (long long)r * p.N + cw + 64 * jj);
+              });
+            });
+          });
+        });
+        __builtin_amdgcn_sched_barrier(0);
+      }
       // one block's results as two 64-byte row chunks per lane (rows64)
       auto chunks = [&](auto ic, auto jc, uint4& ra, uint4& rb) {
         if constexpr (sizeof(TO) == 2) {
@@ -654,8 +745,20 @@ void gemm256_kernel(KParams p) {
                 const uint4 x1 = hh ? rb1 : ra1;              // block j + 1, row r (+ 16)
                 const uint4 recv = xchg8(sel4(hi8, x0, x1));
                 TO* q = rowo + (long long)(32 * i + 16 * hh) * p.ldc + 32 * j;
-                *(uint4*)q = sel4(hi8, recv, x0);                 // row r mod 8 (+ 16)
-                *(uint4*)(q + 8 * p.ldc) = sel4(hi8, x1, recv);   // row 8 + r mod 8 (+ 16)
+                const uint4 c0 = sel4(hi8, recv, x0);             // row r mod 8 (+ 16)
+                const uint4 c1 = sel4(hi8, x1, recv);             // row 8 + r mod 8 (+ 16)
+                if constexpr (APPLY) {
+                  constexpr int jj = j / 2;
+                  const int r0 = wr[i][hh][0], r1 = wr[i][hh][1];
+                  const bool ok0 = (unsigned)r0 < (unsigned)p.wlines, ok1 = (unsigned)r1 < (unsigned)p.wlines;
+                  void* d0 = ok0 ? (void*)(Wb + (long long)r0 * p.N + cw + 64 * jj) : (void*)q;
+                  void* d1 = ok1 ? (void*)(Wb + (long long)r1 * p.N + cw + 64 * jj) : (void*)(q + 8 * p.ldc);
+                  st_nt16(d0, ok0 ? update8<TO>(wv[i][hh][0][jj], c0, p.eta, p.u, p.decay != 0) : c0);
+                  st_nt16(d1, ok1 ? update8<TO>(wv[i][hh][1][jj], c1, p.eta, p.u, p.decay != 0) : c1);
+                } else {
+                  *(uint4*)q = c0;
+                  *(uint4*)(q + 8 * p.ldc) = c1;
+                }
               });
             }
           } else {
@@ -943,6 +1046,15 @@ void gemm256_kernel(KParams p) {
   tile_addr(id, cur);
   if (MULTI && nt > 1) tile_addr(id + G, nxt);
   else nxt = cur;
+  if constexpr (APPLY) {
+    // the first tile's row indices, complete before the first loads of
+    // operands are issued (the compiler does not count those)
+    load_rows(cur, wr);
+#pragma unroll
+    for (int i = 0; i < SUB; ++i)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) asm volatile("" : "+v"(wr[i][hh][0]), "+v"(wr[i][hh][1]));
+  }
   const int KT = p.K / BK;
   const int GT = nt * KT;                     // stages over all tiles (KT >= NBUF when nt > 1)
 
@@ -1071,8 +1183,18 @@ void gemm256_kernel(KParams p) {
       if constexpr (SYM) {
         epi_st = epilogue_sym(cur);
       } else {
-        epilogue_swap(cur);
+        epilogue_swap(cur, nxt, j + 1 < nt);
         epi_st = kEpiStores;
+        if constexpr (APPLY) {
+          static_for<SUB>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            static_for<2>([&](auto hc) {
+              constexpr int hh = decltype(hc)::value;
+              wr[i][hh][0] = wr_next[i][hh][0];
+              wr[i][hh][1] = wr_next[i][hh][1];
+            });
+          });
+        }
       }
       // the next tile's first fragments (after the last tile: an in-bounds
       // read of a buffer no load is writing, unused)
@@ -1085,7 +1207,7 @@ void gemm256_kernel(KParams p) {
     }
   }
 
-  if constexpr (!MULTI) epilogue_swap(cur);
+  if constexpr (!MULTI) epilogue_swap(cur, cur, false);
 }
 
 // Tiles per work-group for the multi-tile large-tile kernel.  A work-group pays the
@@ -1118,10 +1240,36 @@ static long long multi_tile_grid(long long ntiles, int KT, int& per_wg) {
   return (ntiles + per_wg - 1) / per_wg;
 }
 
+// The 256 x 256 tile is used for fp16 / bf16 when the shape is a whole
+// number of tiles and there are at least 128 of them (half the compute units;
+// measured on MI355X, one 4096^2 symmetric product with 136 tiles runs faster
+// on them than with 528 tiles of 128 x 128, one 2048^2 product with 36 does
+// not); otherwise (ragged shapes, small batches, fp32) the 128 x 128 tile.
+static long long tiles_for(const GemmArgs& a, int bm, int& tm, int& tn) {
+  tm = (a.M + bm - 1) / bm;
+  tn = (a.N + bm - 1) / bm;
+  return (long long)(a.op == OP_GEMM ? tm * tn : tm * (tm + 1) / 2) * a.batch;
+}
+
+static bool fast_for(const GemmArgs& a, int bm, int es) {
+  const int BKE = kRowBytes / es, EPC = 16 / es;
+  return a.M % bm == 0 && a.N % bm == 0 && a.K % BKE == 0 && a.lda % EPC == 0 && a.ldb % EPC == 0 &&
+         a.ldc % 8 == 0 && aligned16(a.A) && aligned16(a.B) && aligned16(a.C) &&
+         (a.batch == 1 || (a.sA % EPC == 0 && a.sB % EPC == 0 && a.sC % 8 == 0)) &&
+         (a.E == nullptr || (a.lde % 8 == 0 && aligned16(a.E) && (a.batch == 1 || a.sE % 8 == 0)));
+}
+
+bool gemm_large_tile(const GemmArgs& a) {
+  if (dtype_size(a.dtype) != 2) return false;
+  // the large-tile kernel addresses each operand with 32-bit byte offsets
+  const bool fits32 = (long long)a.M * a.lda * 2 < (1LL << 31) &&
+                      (long long)(a.op == OP_GEMM ? a.K : a.N) * a.ldb * 2 < (1LL << 31);
+  int tm, tn;
+  return fits32 && fast_for(a, 256, 2) && tiles_for(a, 256, tm, tn) >= 128;
+}
+
 template <typename T, typename TO, int OP, int BM>
 static int launch_typed(const GemmArgs& a, hipStream_t s) {
-  constexpr int BKE = kRowBytes / (int)sizeof(T);
-  constexpr int EPC = Mma<T>::EPC;
   constexpr bool HALF = sizeof(T) == 2;
   KParams p;
   p.M = a.M; p.N = a.N; p.K = a.K;
@@ -1131,31 +1279,18 @@ static int launch_typed(const GemmArgs& a, hipStream_t s) {
   p.C = a.C; p.ldc = a.ldc; p.sC = a.sC;
   p.alpha = a.alpha; p.beta = a.beta; p.gamma = a.gamma;
   p.reverse = a.reverse;
+  p.W = a.W; p.sW = a.sW; p.wlines = a.wlines; p.idx = a.idx;
+  p.eta = a.eta; p.u = a.u; p.decay = a.decay;
 
-  // The 256 x 256 tile is used for fp16 / bf16 when the shape is a whole
-  // number of tiles and there are at least 128 of them (half the compute
-  // units; measured on MI355X, one 4096^2 symmetric product with 136 tiles
-  // runs faster on them than with 528 tiles of 128 x 128, one 2048^2 product
-  // with 36 does not); otherwise (ragged shapes, small batches, fp32) the
-  // 128 x 128 tile.
-  auto tiles_for = [&](int bm, int& tm, int& tn) {
-    tm = (a.M + bm - 1) / bm;
-    tn = (a.N + bm - 1) / bm;
-    return (long long)(OP == OP_GEMM ? tm * tn : tm * (tm + 1) / 2) * a.batch;
-  };
-  auto fast_for = [&](int bm) {
-    return a.M % bm == 0 && a.N % bm == 0 && a.K % BKE == 0 && a.lda % EPC == 0 &&
-           a.ldb % EPC == 0 && a.ldc % 8 == 0 && aligned16(a.A) && aligned16(a.B) &&
-           aligned16(a.C) && (a.batch == 1 || (a.sA % EPC == 0 && a.sB % EPC == 0 && a.sC % 8 == 0)) &&
-           (a.E == nullptr || (a.lde % 8 == 0 && aligned16(a.E) && (a.batch == 1 || a.sE % 8 == 0)));
-  };
   int tm, tn;
-  // the large-tile kernel addresses each operand with 32-bit byte offsets
-  const bool fits32 = (long long)a.M * a.lda * 2 < (1LL << 31) &&
-                      (long long)(OP == OP_GEMM ? a.K : a.N) * a.ldb * 2 < (1LL << 31);
-  const bool big = HALF && fits32 && fast_for(256) && tiles_for(256, tm, tn) >= 128;
+  const bool big = HALF && gemm_large_tile(a);
+  // the fused update: large-tile Q X with 16-byte aligned W rows only
+  const bool apply = a.W != nullptr;
+  if (apply && (OP != OP_GEMM || sizeof(TO) != 2 || !big || !a.idx || a.wlines < 1 || !aligned16(a.W) ||
+                (a.batch > 1 && a.sW % 8 != 0)))
+    return DION3_ERR_UNSUPPORTED;
   const int bm = big ? 256 : BM;
-  const long long grid = tiles_for(bm, tm, tn);
+  const long long grid = tiles_for(a, bm, tm, tn);
   p.tiles_m = tm;
   p.tiles_n = tn;
   p.tiles_per_mat = OP == OP_GEMM ? tm * tn : tm * (tm + 1) / 2;
@@ -1168,8 +1303,11 @@ static int launch_typed(const GemmArgs& a, hipStream_t s) {
   }
 
   static const char* names[4] = {"syrk", "sym_sq_add", "sym_mul", "gemm_qx"};
-  TimedLaunch tl(names[OP], s);
-  if (big) {
+  TimedLaunch tl(apply ? "qx_apply" : names[OP], s);
+  if (apply) {
+    if constexpr (OP == OP_GEMM && HALF && sizeof(TO) == 2)
+      (void)launch((gemm256_kernel<T, TO, OP_GEMM, kStages, true>), dim3((unsigned)wgs), dim3(kThreads), s, p);
+  } else if (big) {
     // X X^T without the beta C term is the symmetric product kernel with
     // B = A (same schedule, main loop and epilogue arithmetic; the epilogue
     // operand of beta != 0 costs registers)
@@ -1182,7 +1320,7 @@ static int launch_typed(const GemmArgs& a, hipStream_t s) {
       if (!sym_mul_kernel)
         (void)launch((gemm256_kernel<T, TO, OP, kStages>), dim3((unsigned)wgs), dim3(kThreads), s, p);
     }
-  } else if (fast_for(BM))
+  } else if (fast_for(a, BM, (int)sizeof(T)))
     (void)launch((gemm_kernel<T, TO, OP, false, BM>), dim3((unsigned)grid), dim3(kThreads), s, p);
   else
     (void)launch((gemm_kernel<T, TO, OP, true, BM>), dim3((unsigned)grid), dim3(kThreads), s, p);

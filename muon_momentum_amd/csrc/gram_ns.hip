@@ -52,6 +52,42 @@ static int qx_op(int batch, int k, int m, int in_dtype, const void* Q, long long
   return launch_gemm(g, s);
 }
 
+// The last product O = Q X of a call: one launch, or with fu, one launch per
+// segment, fused with the update of W where the segment asks for it and the
+// large-tile kernel runs the product.
+static int final_qx(int batch, int k, int m, int dt, const void* Q, long long sQ, const void* X, long long sX,
+                    void* O, long long sO, hipStream_t s, bool rev, FusedUpdate* fu) {
+  if (!fu) return qx_op(batch, k, m, dt, Q, sQ, X, sX, dt, O, sO, 1.f, s, rev);
+  const size_t es = dtype_size(dt);
+  int st = DION3_OK;
+  for (int i = 0; i < fu->nseg && st == DION3_OK; ++i) {
+    FusedSegment& g = fu->seg[i];
+    g.fused = false;
+    if (g.nb < 1 || g.b0 < 0 || g.b0 + g.nb > batch) return DION3_ERR_INVALID_ARG;
+    const char* q = (const char*)Q + (size_t)g.b0 * sQ * es;
+    const char* x = (const char*)X + (size_t)g.b0 * sX * es;
+    char* o = (char*)O + (size_t)g.b0 * sO * es;
+    GemmArgs a;
+    a.op = OP_GEMM; a.dtype = dt; a.out_dtype = dt; a.batch = g.nb;
+    a.M = k; a.N = m; a.K = k;
+    a.A = q; a.lda = k; a.sA = sQ;
+    a.B = x; a.ldb = m; a.sB = sX;
+    a.E = nullptr; a.lde = 0; a.sE = 0;
+    a.C = o; a.ldc = m; a.sC = sO;
+    a.alpha = 1.f; a.beta = 0.f; a.gamma = 0.f;
+    a.reverse = rev;
+    if (g.fuse && g.W && g.idx && gemm_large_tile(a)) {
+      a.W = g.W; a.sW = g.sW; a.wlines = g.wlines; a.idx = g.idx;
+      a.eta = fu->eta; a.u = fu->u; a.decay = fu->decay;
+      st = launch_gemm(a, s);
+      g.fused = st == DION3_OK;
+    } else {
+      st = launch_gemm(a, s);
+    }
+  }
+  return st;
+}
+
 static bool ns_dtype_ok(int dt) { return dt == DION3_F16 || dt == DION3_F32 || dt == DION3_BF16; }
 
 }  // namespace dion3
@@ -108,8 +144,9 @@ extern "C" size_t dion3_gram_ns_gathered_workspace_bytes(int batch, int k, int m
   return align256((size_t)batch * k * m * es) + 4 * align256((size_t)batch * k * k * es);
 }
 
-extern "C" int dion3_gram_ns_gathered(int batch, int k, int m, const dion3_ns_params* p, const void* X0,
-                                      void* O, void* ws, size_t ws_bytes, void* stream) {
+namespace dion3 {
+int gram_ns_gathered_fused(int batch, int k, int m, const dion3_ns_params* p, const void* X0, void* O, void* ws,
+                           size_t ws_bytes, void* stream, FusedUpdate* fu) {
   if (batch < 1 || k < 1 || m < 1 || k > m || !p || !X0 || !O || X0 == O) return DION3_ERR_INVALID_ARG;
   if (p->T < 1 || !p->coeffs || !ns_dtype_ok(p->ns_dtype)) return DION3_ERR_INVALID_ARG;
   for (int i = 0; i < 3 * p->T; ++i)
@@ -189,12 +226,21 @@ extern "C" int dion3_gram_ns_gathered(int batch, int k, int m, const dion3_ns_pa
       if (Z != Q) give(Z);
     }
     if (st) break;
-    st = qx_op(batch, k, m, dt, sq[Q], skk, cur, skm, dt, out, skm, 1.f, s, order());
+    if (ps == npass - 1)
+      st = final_qx(batch, k, m, dt, sq[Q], skk, cur, skm, out, skm, s, order(), fu);
+    else
+      st = qx_op(batch, k, m, dt, sq[Q], skk, cur, skm, dt, out, skm, 1.f, s, order());
     give(Q);
     give(R);
     cur = out;
   }
   return st;
+}
+}  // namespace dion3
+
+extern "C" int dion3_gram_ns_gathered(int batch, int k, int m, const dion3_ns_params* p, const void* X0,
+                                      void* O, void* ws, size_t ws_bytes, void* stream) {
+  return gram_ns_gathered_fused(batch, k, m, p, X0, O, ws, ws_bytes, stream, nullptr);
 }
 
 // Gram Newton-Schulz of a group's selected submatrices, from M and the
@@ -264,8 +310,9 @@ extern "C" size_t dion3_standard_ns_workspace_bytes(int batch, int k, int m, int
   return align256((size_t)batch * k * m * es) + 2 * align256((size_t)batch * k * k * es);
 }
 
-extern "C" int dion3_standard_ns(int batch, int k, int m, const dion3_ns_params* p, const void* X0,
-                                 void* O, void* ws, size_t ws_bytes, void* stream) {
+namespace dion3 {
+int standard_ns_fused(int batch, int k, int m, const dion3_ns_params* p, const void* X0, void* O, void* ws,
+                      size_t ws_bytes, void* stream, FusedUpdate* fu) {
   if (batch < 1 || k < 1 || m < 1 || k > m || !p || !X0 || !O || X0 == O) return DION3_ERR_INVALID_ARG;
   if (p->T < 1 || !p->coeffs || !ns_dtype_ok(p->ns_dtype)) return DION3_ERR_INVALID_ARG;
   for (int i = 0; i < 3 * p->T; ++i)
@@ -291,8 +338,16 @@ extern "C" int dion3_standard_ns(int batch, int k, int m, const dion3_ns_params*
     void* out = ((p->T - 1 - t) % 2 == 0) ? O : Xw;
     st = sym_op(OP_SYRK, batch, k, m, dt, cur, skm, cur, skm, nullptr, 0, A, skk, 1.f, 0.f, 0.f, s, order());
     if (!st) st = sym_op(OP_SQ_ADD, batch, k, k, dt, A, skk, A, skk, A, skk, Z, skk, c, b, a, s, order());
-    if (!st) st = qx_op(batch, k, m, dt, Z, skk, cur, skm, dt, out, skm, 1.f, s, order());
+    if (!st)
+      st = t == p->T - 1 ? final_qx(batch, k, m, dt, Z, skk, cur, skm, out, skm, s, order(), fu)
+                         : qx_op(batch, k, m, dt, Z, skk, cur, skm, dt, out, skm, 1.f, s, order());
     cur = out;
   }
   return st;
+}
+}  // namespace dion3
+
+extern "C" int dion3_standard_ns(int batch, int k, int m, const dion3_ns_params* p, const void* X0,
+                                 void* O, void* ws, size_t ws_bytes, void* stream) {
+  return standard_ns_fused(batch, k, m, p, X0, O, ws, ws_bytes, stream, nullptr);
 }

@@ -42,14 +42,6 @@ __device__ __forceinline__ void store8(T* p, const typename Pack8<T>::U& u) {
   }
 }
 
-// w' = round(fp32(a - eta o)) with a = fp32(u w) when decaying, else w.
-template <typename T>
-__device__ __forceinline__ T update_w(T w, float o, float eta, float u, bool decay) {
-  float a = Store<T>::to_f32(w);
-  if (decay) a = u * a;
-  return Store<T>::from_f32(__builtin_fmaf(-eta, o, a));
-}
-
 __device__ __forceinline__ float nscale(const double* sqn, int b, float eps) {
   return (float)(1.0 / (sqrt(sqn[b]) + (double)eps));
 }
@@ -326,8 +318,7 @@ template <typename TS, typename TO>
 static void launch_apply(const dion3_group* g, int axis, int n, int m, void* W, void* M,
                          const int32_t* idx, int k, const void* O, long long ostride, const float* rs,
                          float eta, float wd, float mu, hipStream_t s) {
-  // u = fp32(1 - eta wd): the product is exact in fp64, one rounding to fp32
-  const float u = (float)(1.0 - (double)eta * (double)wd);
+  const float u = weight_decay_factor(eta, wd);
   const int decay = wd != 0.0f;
   TimedLaunch tl(W ? "apply_update" : "decay_rows", s);
   if (decay && W) {
@@ -346,6 +337,20 @@ static void launch_apply(const dion3_group* g, int axis, int n, int m, void* W, 
     dim3 grid((m + 63) / 64, (k + 63) / 64, g->batch);
     (void)launch((apply_cols_kernel<TS, TO>), grid, dim3(256), s, (TS*)W, (TS*)M, g->batch_stride, g->rows, g->cols, idx, k, (const TO*)O, ostride, rs, eta, u, decay, mu);
   }
+}
+
+int decay_unselected(const dion3_group* g, void* W, const int32_t* idx, int k, float u, hipStream_t s) {
+  int n, m, axis;
+  if (!canonical_dims(g, &n, &m, &axis) || !W || !idx || k < 1 || k > n || n > 32768) return DION3_ERR_INVALID_ARG;
+  TimedLaunch tl("apply_update", s);
+  dim3 grid((g->rows + 7) / 8, g->batch);
+  if (g->dtype == DION3_BF16)
+    (void)launch((decay_unselected_kernel<bf16_t>), grid, dim3(256), s, (bf16_t*)W, g->batch_stride, g->rows, g->cols, axis, n, idx, k, u);
+  else if (g->dtype == DION3_F32)
+    (void)launch((decay_unselected_kernel<float>), grid, dim3(256), s, (float*)W, g->batch_stride, g->rows, g->cols, axis, n, idx, k, u);
+  else
+    return DION3_ERR_INVALID_ARG;
+  return launch_status();
 }
 
 // ||M[S,:]||_F^2 per matrix into sqn[batch] (fp64), with line_ws [batch][k]

@@ -256,10 +256,39 @@ static int run_step(int n_groups, const dion3_group* groups, void* const* W, voi
     if (!st && c >= 2) st = stream_wait(side, ev_upd[c - 2]);
     int nb = 0;
     for (int i : cls) nb += groups[i].batch;
+    // Muon flavour with deferred decay (the update leaves M alone): the last
+    // product updates W itself for row-selected bf16 groups, whose O is then
+    // never written or read
+    const bool can_fuse = deferred && !V;
+    std::vector<FusedSegment> segs;
+    FusedUpdate fu{};
+    if (can_fuse) {
+      int b0 = 0;
+      for (int i : cls) {
+        const dion3_group& gi = groups[i];
+        int gn = 0, gm = 0, gax = 0;
+        FusedSegment sg{};
+        sg.b0 = b0;
+        sg.nb = gi.batch;
+        sg.fuse = canonical_dims(&gi, &gn, &gm, &gax) && gax == 0 && gi.dtype == DION3_BF16;
+        sg.W = W[i];
+        sg.sW = gi.batch_stride;
+        sg.wlines = gn;
+        sg.idx = idx[i];
+        segs.push_back(sg);
+        b0 += gi.batch;
+      }
+      fu.nseg = (int)segs.size();
+      fu.seg = segs.data();
+      fu.eta = eta;
+      fu.u = weight_decay_factor(eta, wd);
+      fu.decay = wd != 0.0f;
+    }
     // aspect ratio 1: standard Newton-Schulz on the symmetric kernels (fewer
     // launches, equal work); otherwise Gram Newton-Schulz
-    if (!st) st = mm == kk ? dion3_standard_ns(nb, kk, mm, p, X0buf[c & 1], O, gws, P.gram, side)
-                           : dion3_gram_ns_gathered(nb, kk, mm, p, X0buf[c & 1], O, gws, P.gram, side);
+    FusedUpdate* fup = can_fuse ? &fu : nullptr;
+    if (!st) st = mm == kk ? standard_ns_fused(nb, kk, mm, p, X0buf[c & 1], O, gws, P.gram, side, fup)
+                           : gram_ns_gathered_fused(nb, kk, mm, p, X0buf[c & 1], O, gws, P.gram, side, fup);
     if (!st) st = event_record(ev_ns[c], side);
     // the next class's momentum and gather go ahead of this class's update
     // on the overlapped stream, so that they run beside these products
@@ -268,9 +297,16 @@ static int run_step(int n_groups, const dion3_group* groups, void* const* W, voi
     hipStream_t uc = upd_stream(c);
     if (!st) st = stream_wait(uc, ev_ns[c]);
     nb = 0;
+    int si = 0;
     for (int i : cls) {
       if (st) break;
       const dion3_group& gi = groups[i];
+      if (can_fuse && segs[si++].fused) {
+        // W's selected lines are updated; weight decay of the others remains
+        if (wd != 0.0f) st = decay_unselected(&gi, W[i], idx[i], kk, weight_decay_factor(eta, wd), uc);
+        nb += gi.batch;
+        continue;
+      }
       float* rsc = V ? (float*)(rsc_base + P.rs_off[i]) : nullptr;
       if (V)
         st = dion3_normuon_scale(&gi, idx[i], kk, O + nb * slice, p->ns_dtype, (long long)kk * mm, V[i],

@@ -150,6 +150,42 @@ def test_momentum_rowsel(d, dt, rows, cols, batch, f, axis):
         assert abs(sqn[b] - sq) <= 1e-12 * sq
 
 
+def test_bf16_rounding_special_values(d):
+    """The bf16 rounding of the library's kernels on the momentum pass: exact
+    ties (to even), neighbours of ties, overflow to infinity, subnormal sums
+    and signed zeros equal the oracle's round-once sum bit for bit; a NaN
+    input leaves that NaN quieted, sign and upper payload bits kept (bf16 bits
+    0x7fa1 -> 0x7fe1)."""
+    pairs = [  # (M bits, G bits) in bf16
+        (0x3F80, 0x3B80), (0x3F81, 0x3B80), (0xBF81, 0xBB80), (0x3F80, 0x3B81),
+        (0x3F81, 0x3B7F), (0x4080, 0x3C00), (0x7F7F, 0x7F7F), (0xFF7F, 0xFF7F),
+        (0x7F7F, 0x7B80), (0x0001, 0x0001), (0x0001, 0x8001), (0x8000, 0x8000),
+        (0x0080, 0x8001), (0x007F, 0x0001), (0x3F80, 0xBF80), (0x4B00, 0x3F00),
+    ]
+    nan_pairs = [(0x7FA1, 0x3F80), (0xFFA1, 0x3F80), (0x7FC5, 0x0000), (0x3F80, 0xFFB3)]
+    cols = 64
+    Mb = np.zeros((1, 2, cols), dtype=np.uint16)
+    Gb = np.zeros((1, 2, cols), dtype=np.uint16)
+    for j, (m, g) in enumerate(pairs):
+        Mb[0, 0, j], Gb[0, 0, j] = m, g
+    for j, (m, g) in enumerate(nan_pairs):
+        Mb[0, 1, j], Gb[0, 1, j] = m, g
+    M = torch.from_numpy(Mb.view(np.int16)).view(torch.bfloat16).to(DEV)
+    G = torch.from_numpy(Gb.view(np.int16)).view(torch.bfloat16).to(DEV)
+    Mh, Gh = to64(M), to64(G)
+    idx = torch.empty(1, 1, dtype=torch.int32, device=DEV)
+    d.dion3_momentum_rowsel(M, G, 1, idx)
+    torch.cuda.synchronize()
+    out = bits(M)[0].astype(np.uint16)
+    ref = np_bits(O.momentum_accumulate(Mh[0, 0:1], Gh[0, 0:1], "bf16"), torch.bfloat16).astype(np.uint16)
+    assert np.array_equal(out[0, :len(pairs)], ref[0, :len(pairs)]), (out[0, :len(pairs)], ref[0, :len(pairs)])
+    for j, (m, g) in enumerate(nan_pairs):
+        v = int(out[1, j])
+        print(f"NaN case {m:#06x} + {g:#06x} -> {v:#06x}")
+        nan_in = m if (m & 0x7FFF) > 0x7F80 else g
+        assert v == (nan_in | 0x0040), (hex(m), hex(g), hex(v))
+
+
 def test_rowsel_ties_and_nan(d):
     rows, cols = 40, 96
     g = torch.zeros(1, rows, cols, dtype=torch.float32)

@@ -170,6 +170,49 @@ def test_deferred_decay_matches_immediate(d):
             assert np.array_equal(bits(A[gi][1]), bits(Mb)), (step, gi)
 
 
+@pytest.mark.parametrize("f,wd", [(0.25, 0.0), (0.25, 0.1), (1.0, 0.05)])
+def test_fused_update_matches_immediate(d, f, wd):
+    """Shapes on which the deferred Muon step fuses the update into the last
+    Q X product (row-selected bf16 groups, k and m multiples of 256, at least
+    128 tiles): W, idx and M (once its decay is completed) equal dion3_step's
+    unfused update bit for bit over three steps.  At f = 1/4 the row-selected
+    group shares its Newton-Schulz class with a column-selected one (one fused
+    and one plain segment); at f = 1 the square group runs standard
+    Newton-Schulz with the fused last product."""
+    shapes = [(1024, 4096, 8), (4096, 1024, 4)] if f < 1 else [(1024, 1024, 8), (512, 1024, 2)]
+    dt, mu, eta = "bf16", 0.95, 0.02 / f ** 0.5
+    params = d.make_ns_params(ns_dtype=d.F16)
+    ks = [d.dion3_k_from_fraction(min(r, c), f) for r, c, _ in shapes]
+    A = _groups(shapes, dt, step=0, seed0=80)
+    B = [(W.clone(), M.clone(), G.clone()) for W, M, G in A]
+    idx_a = [torch.empty(b, k, dtype=torch.int32, device=DEV) for (_, _, b), k in zip(shapes, ks)]
+    idx_b = [torch.empty(b, k, dtype=torch.int32, device=DEV) for (_, _, b), k in zip(shapes, ks)]
+    pa = d.StepPlan([g[0] for g in A], [g[1] for g in A], [g[2] for g in A], ks, idx_a, params)
+    pb = d.StepPlan([g[0] for g in B], [g[1] for g in B], [g[2] for g in B], ks, idx_b, params)
+    d.dion3_timing_enable(512)
+    try:
+        for step in range(3):
+            for gi, (r, c, b) in enumerate(shapes):
+                Gn = synth.gradient(r, c, b, dtype=dt, device=DEV, group_seed=80 + gi, step=step + 1)
+                A[gi][2].copy_(Gn)
+                B[gi][2].copy_(Gn)
+            pa.step(eta, wd, mu)
+            pb.step_deferred(eta, wd, mu, has_prev=step > 0)
+            torch.cuda.synchronize()
+            for gi in range(len(shapes)):
+                assert np.array_equal(idx_a[gi].cpu().numpy(), idx_b[gi].cpu().numpy()), (step, gi)
+                assert np.array_equal(bits(A[gi][0]), bits(B[gi][0])), (step, gi)
+                Mb = B[gi][1].clone()
+                d.dion3_decay_rows(Mb, idx_b[gi], ks[gi], mu)
+                torch.cuda.synchronize()
+                assert np.array_equal(bits(A[gi][1]), bits(Mb)), (step, gi)
+        rep = d.dion3_timing_report()
+    finally:
+        d.dion3_timing_enable(0)
+    # the deferred steps did fuse (one fused launch per step)
+    assert rep.get("qx_apply", (0, 0.0))[0] == 3, rep
+
+
 def test_momentum_ef_against_oracle(d):
     """M <- round(round(mu M) + G) on the previous selection, round(M + G) elsewhere."""
     for rows, cols, axis in [(300, 1000, 0), (900, 260, 1)]:
