@@ -278,7 +278,9 @@ extern "C" int dion3_gram_ns(const dion3_group* g, const void* M, const int32_t*
   size_t part[4];
   const size_t need = gram_group_parts(g, k, p, &n, &m, &axis, part);
   if (!need || !M || !idx || !O) return DION3_ERR_INVALID_ARG;
+  // the gather writes X0 in fp16 or fp32 from bf16 or fp32 storage
   if (g->dtype != DION3_F32 && g->dtype != DION3_BF16) return DION3_ERR_INVALID_ARG;
+  if (p->ns_dtype != DION3_F16 && p->ns_dtype != DION3_F32) return DION3_ERR_INVALID_ARG;
   if (p->T < 1 || !p->coeffs || !(p->eps >= 0.f)) return DION3_ERR_INVALID_ARG;
   for (int i = 0; i < 3 * p->T; ++i)
     if (!(p->coeffs[i] == p->coeffs[i])) return DION3_ERR_INVALID_ARG;

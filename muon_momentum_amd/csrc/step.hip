@@ -45,9 +45,12 @@ struct Plan {
 static bool make_plan(int ng, const dion3_group* g, const int* k, const dion3_ns_params* p, Plan& P) {
   if (ng < 1 || !g || !k || !p) return false;
   P.n.resize(ng); P.m.resize(ng); P.axis.resize(ng); P.sqn_off.resize(ng); P.rs_off.resize(ng);
+  // the gather and the update pass take fp16 or fp32 Newton-Schulz buffers
+  // and bf16 or fp32 storage: any other pair is refused here, before any launch
+  if (p->ns_dtype != DION3_F16 && p->ns_dtype != DION3_F32) return false;
   const size_t es = dtype_size(p->ns_dtype);
-  if (!es) return false;
   for (int i = 0; i < ng; ++i) {
+    if (g[i].dtype != DION3_BF16 && g[i].dtype != DION3_F32) return false;
     if (!canonical_dims(&g[i], &P.n[i], &P.m[i], &P.axis[i])) return false;
     if (k[i] < 1 || k[i] > P.n[i]) return false;
     P.rowsel = std::max(P.rowsel, al256(dion3_rowsel_workspace_bytes(&g[i])));

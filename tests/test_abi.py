@@ -220,6 +220,39 @@ def test_group_gram_ns_workspace_and_argument_checks():
     assert L.dion3_gram_ns(ctypes.byref(g16), FAKE, FAKE, 16, pp, P2, FAKE, ws, None) == -1
 
 
+def test_step_refuses_unsupported_type_pairs():
+    """The gather and the update take fp16 or fp32 Newton-Schulz buffers and
+    bf16 or fp32 storage; the whole-step calls and the group form of
+    dion3_gram_ns refuse any other pair in their planning, before any launch
+    (so no M or W is touched)."""
+    L = d.lib
+    ok = d.make_ns_params(ns_dtype=d.F16)
+    b16 = d.make_ns_params(ns_dtype=d.BF16)
+    groups = (d.Group * 2)(d.Group(64, 128, 2, 64 * 128, d.BF16, -1), d.Group(128, 64, 1, 128 * 64, d.BF16, -1))
+    ks = (ctypes.c_int * 2)(16, 16)
+    ptrs = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    sw = L.dion3_step_workspace_bytes(2, groups, ks, ctypes.byref(ok))
+    assert sw > 0
+    assert L.dion3_step_workspace_bytes(2, groups, ks, ctypes.byref(b16)) == 0
+    f16_groups = (d.Group * 2)(d.Group(64, 128, 2, 64 * 128, d.F16, -1), d.Group(128, 64, 1, 128 * 64, d.BF16, -1))
+    assert L.dion3_step_workspace_bytes(2, f16_groups, ks, ctypes.byref(ok)) == 0
+    for gr, p in [(groups, b16), (f16_groups, ok)]:
+        pp = ctypes.byref(p)
+        assert L.dion3_step(2, gr, ptrs, ptrs, ptrs, ks, ptrs, pp, 0.1, 0.0, 0.9, FAKE, sw, None) == -1
+        assert L.dion3_step_deferred(2, gr, ptrs, ptrs, ptrs, ks, ptrs, 1, pp, 0.1, 0.0, 0.9, FAKE, sw, None) == -1
+        vs = (ctypes.c_void_p * 2)(0x3000, 0x4000)
+        assert L.dion3_step_normuon(2, gr, ptrs, ptrs, ptrs, ks, ptrs, vs, 1, 1, pp, 0.1, 0.0, 0.9, 0.95, 1e-8,
+                                    FAKE, sw, None) == -1
+        out = ctypes.c_void_p()
+        assert L.dion3_step_graph_create(2, gr, ptrs, ptrs, ptrs, ks, ptrs, 1, pp, 0.1, 0.0, 0.9, FAKE, sw,
+                                         ctypes.byref(out)) == -1
+        assert out.value is None
+    g = d.Group(64, 300, 2, 64 * 300, d.BF16, -1)
+    ws = L.dion3_gram_ns_workspace_bytes(ctypes.byref(g), 16, ctypes.byref(b16))
+    assert L.dion3_gram_ns(ctypes.byref(g), FAKE, FAKE, 16, ctypes.byref(b16), ctypes.c_void_p(0x2000), FAKE, ws,
+                           None) == -1
+
+
 def test_release_without_gpu_work_is_a_no_op():
     """dion3_release frees only what the library created; with nothing created
     it makes no HIP call and succeeds (twice in a row as well)."""
