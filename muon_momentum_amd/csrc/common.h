@@ -239,8 +239,9 @@ struct GemmArgs {
 };
 
 int launch_gemm(const GemmArgs& a, hipStream_t s);
-// Whether launch_gemm runs `a` on the large-tile kernel (the only one that
-// can fuse the update).
+// Whether launch_gemm runs `a` on the large-tile kernel, and whether it can
+// fuse the update into it (large tiles, 16-bit result, 16-byte aligned W rows).
 bool gemm_large_tile(const GemmArgs& a);
+bool gemm_fused_update_ok(const GemmArgs& a);
 
 }  // namespace dion3

@@ -1268,6 +1268,11 @@ bool gemm_large_tile(const GemmArgs& a) {
   return fits32 && fast_for(a, 256, 2) && tiles_for(a, 256, tm, tn) >= 128;
 }
 
+bool gemm_fused_update_ok(const GemmArgs& a) {
+  return a.op == OP_GEMM && dtype_size(a.out_dtype) == 2 && gemm_large_tile(a) && a.W && a.idx &&
+         a.wlines >= 1 && aligned16(a.W) && (a.batch == 1 || a.sW % 8 == 0);
+}
+
 template <typename T, typename TO, int OP, int BM>
 static int launch_typed(const GemmArgs& a, hipStream_t s) {
   constexpr bool HALF = sizeof(T) == 2;
@@ -1286,9 +1291,7 @@ static int launch_typed(const GemmArgs& a, hipStream_t s) {
   const bool big = HALF && gemm_large_tile(a);
   // the fused update: large-tile Q X with 16-byte aligned W rows only
   const bool apply = a.W != nullptr;
-  if (apply && (OP != OP_GEMM || sizeof(TO) != 2 || !big || !a.idx || a.wlines < 1 || !aligned16(a.W) ||
-                (a.batch > 1 && a.sW % 8 != 0)))
-    return DION3_ERR_UNSUPPORTED;
+  if (apply && (!HALF || !gemm_fused_update_ok(a))) return DION3_ERR_UNSUPPORTED;
   const int bm = big ? 256 : BM;
   const long long grid = tiles_for(a, bm, tm, tn);
   p.tiles_m = tm;

@@ -76,10 +76,11 @@ static int final_qx(int batch, int k, int m, int dt, const void* Q, long long sQ
     a.C = o; a.ldc = m; a.sC = sO;
     a.alpha = 1.f; a.beta = 0.f; a.gamma = 0.f;
     a.reverse = rev;
-    if (g.fuse && g.W && g.idx && gemm_large_tile(a)) {
-      a.W = g.W; a.sW = g.sW; a.wlines = g.wlines; a.idx = g.idx;
-      a.eta = fu->eta; a.u = fu->u; a.decay = fu->decay;
-      st = launch_gemm(a, s);
+    GemmArgs f = a;
+    f.W = g.W; f.sW = g.sW; f.wlines = g.wlines; f.idx = g.idx;
+    f.eta = fu->eta; f.u = fu->u; f.decay = fu->decay;
+    if (g.fuse && gemm_fused_update_ok(f)) {
+      st = launch_gemm(f, s);
       g.fused = st == DION3_OK;
     } else {
       st = launch_gemm(a, s);

@@ -213,6 +213,47 @@ def test_fused_update_matches_immediate(d, f, wd):
     assert rep.get("qx_apply", (0, 0.0))[0] == 3, rep
 
 
+def test_fused_update_falls_back_on_unaligned_rows(d):
+    """A row-selected group whose matrices are not 16-byte aligned (batch
+    stride padded by 3 elements) cannot take the fused update: the deferred
+    step runs the plain last product and the apply pass instead, and still
+    equals dion3_step bit for bit."""
+    r, c, b, f = 1024, 4096, 8, 0.25
+    mu, eta = 0.95, 0.04
+    stride = r * c + 3
+    params = d.make_ns_params(ns_dtype=d.F16)
+    k = d.dion3_k_from_fraction(r, f)
+
+    def strided(t):
+        buf = torch.zeros(b * stride, dtype=t.dtype, device=DEV)
+        v = buf.as_strided((b, r, c), (stride, c, 1))
+        v.copy_(t)
+        return v
+
+    (W0, M0, G0), = _groups([(r, c, b)], "bf16", step=0, seed0=120)
+    A = [strided(W0), strided(M0), strided(G0)]
+    B = [strided(W0), strided(M0), strided(G0)]
+    idx_a = torch.empty(b, k, dtype=torch.int32, device=DEV)
+    idx_b = torch.empty(b, k, dtype=torch.int32, device=DEV)
+    pa = d.StepPlan([A[0]], [A[1]], [A[2]], [k], [idx_a], params)
+    pb = d.StepPlan([B[0]], [B[1]], [B[2]], [k], [idx_b], params)
+    d.dion3_timing_enable(256)
+    try:
+        for step in range(2):
+            Gn = synth.gradient(r, c, b, dtype="bf16", device=DEV, group_seed=120, step=step + 1)
+            A[2].copy_(Gn)
+            B[2].copy_(Gn)
+            pa.step(eta, 0.0, mu)
+            pb.step_deferred(eta, 0.0, mu, has_prev=step > 0)
+            torch.cuda.synchronize()
+            assert torch.equal(idx_a, idx_b), step
+            assert np.array_equal(bits(A[0]), bits(B[0])), step
+        rep = d.dion3_timing_report()
+    finally:
+        d.dion3_timing_enable(0)
+    assert "qx_apply" not in rep, rep
+
+
 def test_momentum_ef_against_oracle(d):
     """M <- round(round(mu M) + G) on the previous selection, round(M + G) elsewhere."""
     for rows, cols, axis in [(300, 1000, 0), (900, 260, 1)]:
