@@ -275,32 +275,35 @@ def run_step_bench(d, synth, torch, args):
            "p90": per_step[min(len(per_step) - 1, int(math.ceil(0.9 * len(per_step))) - 1)]}
     print(f"# timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
 
-    # the same step as one HIP graph (dion3_step_graph_create): enqueue time of
-    # one launch and K launches timed as above
+    # the same step as HIP graphs (dion3_step_graph_create): per-stream
+    # segments replayed on the library's streams ("graph"), and one graph of
+    # the whole step ("graph_one"); enqueue time of one launch and K launches
+    # timed as above
     if args.flavor == "muon" and not args.no_graph:
-        graph = plan.graph(eta, 0.0, MU, has_prev=True)
-        for _ in range(3):
-            graph.launch()
-        ghost = []
-        for _ in range(5):
+        for key, one in (("graph", False), ("graph_one", True)):
+            graph = plan.graph(eta, 0.0, MU, has_prev=True, one=one)
+            for _ in range(3):
+                graph.launch()
+            ghost = []
+            for _ in range(5):
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                graph.launch()
+                ghost.append(1e3 * (time.perf_counter() - t0))
             torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            graph.launch()
-            ghost.append(1e3 * (time.perf_counter() - t0))
-        torch.cuda.synchronize()
-        ev[0].record()
-        for i in range(args.steps):
-            graph.launch()
-            ev[i + 1].record()
-        torch.cuda.synchronize()
-        gper = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
-        pct["graph"] = {"ms_per_step": round(ev[0].elapsed_time(ev[-1]) / args.steps, 3),
+            ev[0].record()
+            for i in range(args.steps):
+                graph.launch()
+                ev[i + 1].record()
+            torch.cuda.synchronize()
+            gper = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+            pct[key] = {"ms_per_step": round(ev[0].elapsed_time(ev[-1]) / args.steps, 3),
                         "ms_per_step_p50": round(gper[len(gper) // 2], 3),
                         "host_ms_per_step": round(sorted(ghost)[len(ghost) // 2], 3)}
-        graph.destroy()
-        torch.cuda.synchronize()
-        print(f"# graph {args.steps} steps: {pct['graph']['ms_per_step']:.3f} ms/step", file=sys.stderr,
-              flush=True)
+            graph.destroy()
+            torch.cuda.synchronize()
+            print(f"# {key} {args.steps} steps: {pct[key]['ms_per_step']:.3f} ms/step", file=sys.stderr,
+                  flush=True)
 
     # a separate instrumented pass for the per-kernel table: a HIP event pair
     # around every library launch, on the stream of the launch
@@ -436,6 +439,7 @@ def main():
         "ms_per_step_instrumented": round(pct["instrumented"], 3),
         "profile_steps": pct["profile_steps"],
         "graph": pct.get("graph"),
+        "graph_one": pct.get("graph_one"),
         "data": "synthetic (Gaussian gradients with log-normal line scales, seeded)",
         "config": {"workload": f"{args.set} shape set Dion3 step, f={args.f:g}"
                                + ("" if args.flavor == "muon" else ", NorMuon flavour"),

@@ -324,25 +324,37 @@ int dion3_step_deferred(int n_groups, const dion3_group* groups, void* const* W,
                         const dion3_ns_params* p, float eta, float wd, float mu,
                         void* ws, size_t ws_bytes, void* stream);
 
-/* The deferred step as a HIP graph (Section 6: the step's launches have the
- * same dependencies every step, so one recorded graph replaces them; the
- * pages replay it to cut the host time per step).  The graph is built node by
- * node, not by stream capture: every launch of dion3_step_deferred with these
- * arguments becomes a kernel node, and the order its streams and events give
- * becomes node dependencies.  It is instantiated once; each dion3_graph_launch
- * then performs exactly that step (same pointers, scalars and has_prev; the
- * buffers' current contents) on `stream`, ordered like any other work there,
- * with one host call.  Creation allocates the graph; launching allocates
- * nothing.  Results are bit-identical to the eager call.  A graph must not
- * be launched while another launch of it, or an eager step on the same
- * tensors or workspace, may run concurrently.  Steady state: run the first
- * step eagerly (has_prev = 0), then launch a graph created with has_prev = 1
- * every step. */
+/* The deferred step as HIP graphs (Section 6: the step's launches have the
+ * same dependencies every step, so recorded graphs replace them; the pages
+ * replay the step to cut the host time per step).  Nothing is recorded by
+ * stream capture: dion3_step_deferred runs once with these arguments while
+ * its launches are collected; the kernels one stream receives between two
+ * event operations on that stream become one graph (kernel nodes in a
+ * chain), instantiated once.  dion3_graph_launch replays the step in the
+ * driver's order: each such graph launched on its stream (`stream` for the
+ * caller's part, the library's streams, with their compute-unit masks, for
+ * the rest) and the driver's event records and waits between them, about a
+ * tenth of the eager call's host calls.  It performs exactly that step (same
+ * pointers, scalars and has_prev; the buffers' current contents), ordered
+ * after earlier work on `stream`; the returned work is complete once
+ * `stream` reaches it.  Creation allocates the graphs; launching allocates
+ * nothing.  Results are bit-identical to the eager call.  Launch on the
+ * device the graph was created on (else DION3_ERR_INVALID_ARG); after
+ * dion3_release the graph cannot be launched (DION3_ERR_INVALID_ARG) and
+ * should be destroyed.  A graph must not be launched while another launch of
+ * it, or an eager step on the same tensors or workspace, may run
+ * concurrently.  Steady state: run the first step eagerly (has_prev = 0),
+ * then launch a graph created with has_prev = 1 every step.
+ * flags: 0, or DION3_GRAPH_ONE for a single graph of the whole step whose
+ * stream branches HIP schedules itself (one host call per step; the
+ * library's streams and compute-unit masks are not used; faster for small
+ * steps, slower for large ones).  Other bits: DION3_ERR_INVALID_ARG. */
+#define DION3_GRAPH_ONE 1u
 typedef struct dion3_graph_s* dion3_graph;
 int dion3_step_graph_create(int n_groups, const dion3_group* groups, void* const* W, void* const* M,
                             const void* const* G, const int* k, int32_t* const* idx, int has_prev,
                             const dion3_ns_params* p, float eta, float wd, float mu,
-                            void* ws, size_t ws_bytes, dion3_graph* out);
+                            void* ws, size_t ws_bytes, unsigned flags, dion3_graph* out);
 int dion3_graph_launch(dion3_graph g, void* stream);
 int dion3_graph_destroy(dion3_graph g);
 

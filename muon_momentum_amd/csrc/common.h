@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <tuple>
 #include <utility>
 
@@ -183,6 +184,10 @@ int run_step_deferred(int n_groups, const dion3_group* groups, void* const* W, v
                       const dion3_ns_params* p, float eta, float wd, float mu, void* ws, size_t ws_bytes,
                       void* stream);
 int event_record(hipEvent_t e, hipStream_t s);
+// The lock the step driver holds while it enqueues (step.hip), and the
+// generation of the current device's library streams (0: none yet or released).
+std::mutex& side_mutex();
+unsigned side_generation();
 
 // u = fp32(1 - eta wd): the product is exact in fp64, one rounding to fp32
 inline float weight_decay_factor(float eta, float wd) { return (float)(1.0 - (double)eta * (double)wd); }

@@ -83,10 +83,22 @@ struct SideCtx {
   hipStream_t side = nullptr;   // gathers + Newton-Schulz, every compute unit (non-blocking)
   hipStream_t mem = nullptr;    // overlapped HBM-bound passes, half the compute units (blocking)
   std::vector<hipEvent_t> ev;
+  unsigned gen = 0;             // set when the streams are created (step graphs check it)
 };
 constexpr int kMaxDevices = 64;
 static std::mutex g_side_mu;
 static SideCtx g_side[kMaxDevices];
+static unsigned g_side_gen = 0;
+
+std::mutex& side_mutex() { return g_side_mu; }
+
+// Generation of the current device's library streams (0: none); the caller
+// holds side_mutex().
+unsigned side_generation() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  return g_side[dev].side ? g_side[dev].gen : 0;
+}
 
 // Compute-unit mask of the overlapped stream: unit i is used when
 // (i mod 8 + i div 8) mod 8 < 4, which takes half of the units of every XCD
@@ -106,9 +118,12 @@ static int side_ctx(size_t nev, SideCtx** out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DION3_ERR_HIP;
   SideCtx& c = g_side[dev];
-  if (!c.side && hipStreamCreateWithFlags(&c.side, hipStreamNonBlocking) != hipSuccess) {
-    c.side = nullptr;
-    return DION3_ERR_HIP;
+  if (!c.side) {
+    if (hipStreamCreateWithFlags(&c.side, hipStreamNonBlocking) != hipSuccess) {
+      c.side = nullptr;
+      return DION3_ERR_HIP;
+    }
+    c.gen = ++g_side_gen;
   }
   if (!c.mem && make_mem_stream(dev, &c.mem) != DION3_OK) {
     c.mem = nullptr;

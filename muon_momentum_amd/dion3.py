@@ -20,6 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("DION3_LIB") or os.path.join(_HERE, "libdion3.so")
 
 F32, F16, BF16 = 0, 1, 2
+GRAPH_ONE = 1                    # DION3_GRAPH_ONE
 _TORCH_TO_DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 _DT_TO_TORCH = {v: k for k, v in _TORCH_TO_DT.items()}
 
@@ -90,7 +91,7 @@ def _load() -> ctypes.CDLL:
                            ctypes.POINTER(i), ctypes.POINTER(vp), pp, f, f, f, vp, sz, vp]),
         "dion3_step_graph_create": (i, [i, gp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
                                         ctypes.POINTER(i), ctypes.POINTER(vp), i, pp, f, f, f, vp, sz,
-                                        ctypes.POINTER(vp)]),
+                                        ctypes.c_uint, ctypes.POINTER(vp)]),
         "dion3_graph_launch": (i, [vp, vp]),
         "dion3_graph_destroy": (i, [vp]),
         "dion3_timing_enable": (i, [i]),
@@ -358,13 +359,15 @@ class StepPlan:
                                       eta, wd, mu, beta2, nm_eps, _ptr(self.ws), self.ws.numel(),
                                       _stream()), "dion3_step_normuon")
 
-    def graph(self, eta, wd, mu, has_prev=True):
-        """dion3_step_graph_create: the deferred step as an instantiated HIP
-        graph over this plan's tensors and workspace (StepGraph)."""
+    def graph(self, eta, wd, mu, has_prev=True, one=False):
+        """dion3_step_graph_create: the deferred step as instantiated HIP graphs
+        over this plan's tensors and workspace (StepGraph); one=True builds
+        the single-graph form (DION3_GRAPH_ONE)."""
         g = ctypes.c_void_p()
         _check(lib.dion3_step_graph_create(self.n, self.groups, self.W, self.M, self.G, self.k, self.idx,
                                            1 if has_prev else 0, ctypes.byref(self.params), eta, wd, mu,
-                                           _ptr(self.ws), self.ws.numel(), ctypes.byref(g)),
+                                           _ptr(self.ws), self.ws.numel(), GRAPH_ONE if one else 0,
+                                           ctypes.byref(g)),
                "dion3_step_graph_create")
         return StepGraph(g, self)
 

@@ -244,7 +244,7 @@ def test_step_refuses_unsupported_type_pairs():
         assert L.dion3_step_normuon(2, gr, ptrs, ptrs, ptrs, ks, ptrs, vs, 1, 1, pp, 0.1, 0.0, 0.9, 0.95, 1e-8,
                                     FAKE, sw, None) == -1
         out = ctypes.c_void_p()
-        assert L.dion3_step_graph_create(2, gr, ptrs, ptrs, ptrs, ks, ptrs, 1, pp, 0.1, 0.0, 0.9, FAKE, sw,
+        assert L.dion3_step_graph_create(2, gr, ptrs, ptrs, ptrs, ks, ptrs, 1, pp, 0.1, 0.0, 0.9, FAKE, sw, 0,
                                          ctypes.byref(out)) == -1
         assert out.value is None
     g = d.Group(64, 300, 2, 64 * 300, d.BF16, -1)
@@ -272,13 +272,14 @@ def test_step_graph_argument_checks():
     sw = L.dion3_step_workspace_bytes(2, groups, ks, pp)
     out = ctypes.c_void_p()
     args = (ptrs, ptrs, ptrs, ks, ptrs, 1, pp, 0.1, 0.0, 0.9)
-    assert L.dion3_step_graph_create(2, groups, *args, FAKE, sw - 1, ctypes.byref(out)) == -3
-    assert L.dion3_step_graph_create(2, groups, *args, FAKE, sw, None) == -1
+    assert L.dion3_step_graph_create(2, groups, *args, FAKE, sw - 1, 0, ctypes.byref(out)) == -3
+    assert L.dion3_step_graph_create(2, groups, *args, FAKE, sw, 0, None) == -1
+    assert L.dion3_step_graph_create(2, groups, *args, FAKE, sw, 2, ctypes.byref(out)) == -1   # unknown flag
     bad = (ctypes.c_int * 2)(16, 65)
-    assert L.dion3_step_graph_create(2, groups, ptrs, ptrs, ptrs, bad, ptrs, 1, pp, 0.1, 0.0, 0.9, FAKE, sw,
+    assert L.dion3_step_graph_create(2, groups, ptrs, ptrs, ptrs, bad, ptrs, 1, pp, 0.1, 0.0, 0.9, FAKE, sw, 0,
                                      ctypes.byref(out)) == -1
     nulls = (ctypes.c_void_p * 2)(0x1000, None)
-    assert L.dion3_step_graph_create(2, groups, nulls, ptrs, ptrs, ks, ptrs, 1, pp, 0.1, 0.0, 0.9, FAKE, sw,
+    assert L.dion3_step_graph_create(2, groups, nulls, ptrs, ptrs, ks, ptrs, 1, pp, 0.1, 0.0, 0.9, FAKE, sw, 0,
                                      ctypes.byref(out)) == -1
     assert out.value is None
     assert L.dion3_graph_launch(None, None) == -1

@@ -1,6 +1,8 @@
-"""The deferred step as a HIP graph built node by node (no stream capture;
+"""The deferred step as HIP graphs built node by node (no stream capture;
 "Dion3: Full-Stack Orthogonal Updates", Section 6: the step's launches have
-the same dependencies every step, so one graph is replayed per step).
+the same dependencies every step, so recorded graphs are replayed per step),
+in both forms: per-stream segments replayed on the library's streams, and
+one graph of the whole step.
 
 A graph is created once over one set of tensors and replayed several times;
 between replays new gradients are copied in and the same step runs eagerly on
@@ -35,7 +37,7 @@ def _state(shapes, ks, seed0=0):
     return Ws, Ms, Gs, ids
 
 
-def _replays_match(d, shapes, f, replays, seed0=0):
+def _replays_match(d, shapes, f, replays, seed0=0, one=False):
     ks = [d.dion3_k_from_fraction(min(r, c), f) for r, c, _ in shapes]
     mu, eta = 0.95, 0.02 / math.sqrt(f)
     params = d.make_ns_params(ns_dtype=d.F16)
@@ -46,7 +48,7 @@ def _replays_match(d, shapes, f, replays, seed0=0):
     pa.step_deferred(eta, 0.0, mu, has_prev=False)
     pb.step_deferred(eta, 0.0, mu, has_prev=False)
     torch.cuda.synchronize()
-    graph = pb.graph(eta, 0.0, mu, has_prev=True)
+    graph = pb.graph(eta, 0.0, mu, has_prev=True, one=one)
     torch.cuda.synchronize()
     for step in range(1, replays + 1):
         for gi, (r, c, b) in enumerate(shapes):
@@ -67,14 +69,17 @@ def _replays_match(d, shapes, f, replays, seed0=0):
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("one", [False, True])
 @pytest.mark.parametrize("f", [0.25, 1.0])
-def test_step_graph_replays_match_eager(d, f):
+def test_step_graph_replays_match_eager(d, f, one):
     # three (k, m) classes (rows and columns selected together), a square class
-    # at f = 1, and 256 x 256 tiles (the 1024-row groups)
-    _replays_match(d, [(256, 1024, 6), (1024, 256, 3), (512, 512, 2), (1024, 2048, 2)], f, replays=4)
+    # at f = 1, and 256 x 256 tiles (the 1024-row groups); the segmented and
+    # the single-graph form
+    _replays_match(d, [(256, 1024, 6), (1024, 256, 3), (512, 512, 2), (1024, 2048, 2)], f, replays=4, one=one)
 
 
+@pytest.mark.parametrize("one", [False, True])
 @pytest.mark.timeout(600)
-def test_step_graph_7b_matches_eager(d):
+def test_step_graph_7b_matches_eager(d, one):
     """The benchmarked workload: 7B shape set, f = 1/4, two replays."""
-    _replays_match(d, synth.shape_groups("7b"), 0.25, replays=2, seed0=0)
+    _replays_match(d, synth.shape_groups("7b"), 0.25, replays=2, seed0=0, one=one)
