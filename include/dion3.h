@@ -71,6 +71,14 @@ typedef struct {
   int ns_dtype;
 } dion3_ns_params;
 
+/* Optional finite check (Appendix B, Figure 11: the half-precision Gram
+ * iteration without restarts ends with non-finite outputs).  Adds the number
+ * of NaN and +-Inf entries of x (n elements of dtype DION3_F32, DION3_F16 or
+ * DION3_BF16, device memory, any alignment) to *count, a device uint64 the
+ * caller zeroes beforehand; asynchronous on `stream`, allocates nothing.
+ * DION3_ERR_INVALID_ARG for a null pointer, n == 0 or another dtype. */
+int dion3_count_nonfinite(const void* x, int dtype, size_t n, unsigned long long* count, void* stream);
+
 /* ---------------------------------------------------------------- helpers */
 
 /* k = ceil(f * n) for the exact product of the given double f and n, clamped

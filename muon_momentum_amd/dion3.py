@@ -93,6 +93,7 @@ def _load() -> ctypes.CDLL:
                                         ctypes.POINTER(i), ctypes.POINTER(vp), i, pp, f, f, f, vp, sz,
                                         ctypes.c_uint, ctypes.POINTER(vp)]),
         "dion3_graph_launch": (i, [vp, vp]),
+        "dion3_count_nonfinite": (i, [vp, i, sz, vp, vp]),
         "dion3_graph_destroy": (i, [vp]),
         "dion3_timing_enable": (i, [i]),
         "dion3_timing_report": (i, [ctypes.c_char_p, sz]),
@@ -405,6 +406,22 @@ class StepGraph:
 def dion3_step(Ws, Ms, Gs, ks, idxs, eta, wd, mu, params=None, sel_axes=None):
     p = params if params is not None else make_ns_params()
     StepPlan(Ws, Ms, Gs, ks, idxs, p, sel_axes).step(eta, wd, mu)
+
+
+def dion3_count_nonfinite(x, count=None) -> int:
+    """Number of NaN / +-Inf entries of the device tensor x (fp32, fp16 or
+    bf16).  With a caller-zeroed int64 device tensor `count` the call only
+    enqueues (the library adds to it) and returns None; otherwise it uses a
+    fresh counter and reads it back."""
+    t = x.detach()
+    if not t.is_contiguous():
+        raise Dion3Error("dion3_count_nonfinite: x must be contiguous")
+    own = count is None
+    if own:
+        count = torch.zeros(1, dtype=torch.int64, device=t.device)
+    _check(lib.dion3_count_nonfinite(_ptr(t), dtype_code(t.dtype), t.numel(), _ptr(count), _stream()),
+           "dion3_count_nonfinite")
+    return int(count.item()) if own else None
 
 
 def dion3_timing_enable(max_launches: int) -> None:

@@ -253,6 +253,15 @@ def test_step_refuses_unsupported_type_pairs():
                            None) == -1
 
 
+def test_count_nonfinite_argument_checks():
+    """The finite check validates before any launch: pointers, n and dtype."""
+    L = d.lib
+    assert L.dion3_count_nonfinite(None, d.F32, 10, FAKE, None) == -1
+    assert L.dion3_count_nonfinite(FAKE, d.F32, 10, None, None) == -1
+    assert L.dion3_count_nonfinite(FAKE, d.F32, 0, FAKE, None) == -1
+    assert L.dion3_count_nonfinite(FAKE, 7, 10, FAKE, None) == -1
+
+
 def test_release_without_gpu_work_is_a_no_op():
     """dion3_release frees only what the library created; with nothing created
     it makes no HIP call and succeeds (twice in a row as well)."""

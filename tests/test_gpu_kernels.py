@@ -471,3 +471,30 @@ def test_products_independent_of_batch(d):
     d.dion3_gemm(Q[3:4], X[3:4], Y1, 1.0)
     torch.cuda.synchronize()
     assert torch.equal(Y[3].view(torch.int16), Y1[0].view(torch.int16)), "gemm"
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_count_nonfinite(d, dt):
+    """dion3_count_nonfinite counts NaN and +-Inf entries exactly: planted at
+    random positions of ragged sizes, on aligned and misaligned starts
+    (vector and scalar paths), against torch.isfinite; finite extremes (the
+    largest finite value, subnormals) are not counted."""
+    g = torch.Generator().manual_seed(11)
+    big = torch.finfo(TD[dt]).max
+    for n in [1, 7, 1000, (1 << 20) + 3]:
+        x = torch.randn(n + 1, generator=g).to(TD[dt])
+        x[torch.randint(0, n + 1, (max(1, n // 97),), generator=g)] = float("nan")
+        x[torch.randint(0, n + 1, (max(1, n // 131),), generator=g)] = float("inf")
+        x[torch.randint(0, n + 1, (max(1, n // 173),), generator=g)] = float("-inf")
+        x[torch.randint(0, n + 1, (max(1, n // 191),), generator=g)] = big
+        x[torch.randint(0, n + 1, (max(1, n // 211),), generator=g)] = torch.finfo(TD[dt]).tiny / 4
+        xd = x.to(DEV)
+        for view in (xd[:n], xd[1:]):          # 16-byte aligned start, then a misaligned one
+            want = int((~torch.isfinite(view.cpu().float())).sum())
+            assert d.dion3_count_nonfinite(view.contiguous() if not view.is_contiguous() else view) == want, (n, want)
+        # accumulation into a caller counter across two calls
+        cnt = torch.zeros(1, dtype=torch.int64, device=DEV)
+        d.dion3_count_nonfinite(xd[:n], cnt)
+        d.dion3_count_nonfinite(xd[1:], cnt)
+        torch.cuda.synchronize()
+        assert int(cnt.item()) == int((~torch.isfinite(x[:n].float())).sum()) + int((~torch.isfinite(x[1:].float())).sum())
