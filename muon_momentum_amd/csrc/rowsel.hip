@@ -68,12 +68,14 @@ __global__ __launch_bounds__(256) void momentum_rows_kernel(
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r0 = (blockIdx.x * 4 + wave) * kRowsPerWave;
+  // rows selected by the previous step (decay still pending): one search for
+  // the wave's first row, then a walk along the ascending selection
+  const int32_t* pb = pidx ? pidx + (long long)b * pk : nullptr;
+  int pos = pidx ? lower_bound_i32(pb, pk, r0) : 0;
   for (int r = r0; r < r0 + kRowsPerWave && r < rows; ++r) {
-    // was this row selected by the previous step (decay still pending)?
     bool dec = false;
     if (pidx) {
-      const int32_t* pb = pidx + (long long)b * pk;
-      const int pos = lower_bound_i32(pb, pk, r);
+      while (pos < pk && pb[pos] < r) ++pos;
       dec = pos < pk && pb[pos] == r;
     }
     T* mr = M + b * bstride + (long long)r * cols;
