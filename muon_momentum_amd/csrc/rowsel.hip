@@ -10,7 +10,7 @@
 // the fp64 sums of |M| (the key) and M^2 (for the Frobenius norm of the
 // selected submatrix).  Row selection: one wave per row, lane-sequential
 // accumulation then a butterfly reduction.  Column selection: a work-group
-// owns 512 columns x 1024 rows; each lane owns 8 columns; the four waves are
+// owns 512 columns x 512 rows; each lane owns 8 columns; the four waves are
 // combined in a fixed order and written as per-chunk partial sums.
 // Kernel 2 (one work-group per matrix): sums the partials in chunk order,
 // radix-selects the k-th largest key on its 64-bit pattern (non-negative
@@ -25,7 +25,7 @@
 namespace dion3 {
 
 constexpr int kColBlock = 512;     // columns per work-group (column selection)
-constexpr int kChunkRows = 1024;   // rows per work-group (column selection)
+constexpr int kChunkRows = 512;    // rows per work-group (column selection)
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkPer = 32;       // keys per thread -> n <= 32768
 constexpr int kRowsPerWave = 2;
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(256) void momentum_cols_kernel(
   const int rend = min(rbeg + kChunkRows, rows);
   T* Mb = M + b * bstride;
   const T* Gb = G + b * bstride;
-#pragma unroll 2
+#pragma unroll 4
   for (int r = rbeg + wave; r < rend; r += 4) {
     T* mr = Mb + (long long)r * cols;
     const T* gr = Gb + (long long)r * cols;
