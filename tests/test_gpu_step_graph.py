@@ -83,3 +83,28 @@ def test_step_graph_replays_match_eager(d, f, one):
 def test_step_graph_7b_matches_eager(d, one):
     """The benchmarked workload: 7B shape set, f = 1/4, two replays."""
     _replays_match(d, synth.shape_groups("7b"), 0.25, replays=2, seed0=0, one=one)
+
+
+def test_step_graph_after_release(d):
+    """dion3_release destroys the library's streams: a segmented graph built
+    on them then refuses to launch (DION3_ERR_INVALID_ARG, nothing enqueued),
+    while the single-graph form, which uses no library stream, still runs;
+    the next eager step recreates the streams."""
+    shapes = [(256, 1024, 2)]
+    ks = [d.dion3_k_from_fraction(256, 0.25)]
+    params = d.make_ns_params(ns_dtype=d.F16)
+    A = _state(shapes, ks)
+    plan = d.StepPlan(A[0], A[1], A[2], ks, A[3], params)
+    plan.step_deferred(0.04, 0.0, 0.95, has_prev=False)
+    g_seg = plan.graph(0.04, 0.0, 0.95, has_prev=True)
+    g_one = plan.graph(0.04, 0.0, 0.95, has_prev=True, one=True)
+    torch.cuda.synchronize()
+    assert d.lib.dion3_release() == 0
+    with pytest.raises(d.Dion3Error, match=r"\(-1\)"):
+        g_seg.launch()
+    g_one.launch()
+    torch.cuda.synchronize()
+    plan.step_deferred(0.04, 0.0, 0.95, has_prev=True)
+    torch.cuda.synchronize()
+    g_seg.destroy()
+    g_one.destroy()
