@@ -351,3 +351,63 @@ def test_resume_round_trip_matches_straight_run(d):
     torch.cuda.synchronize()
     for gi in range(len(shapes)):
         assert np.array_equal(bits(A[gi][1]), bits(B[gi][1])), gi
+
+
+def test_concurrent_callers_match_sequential(d):
+    """Two host threads, each with its own stream and tensors, enqueue three
+    deferred steps at the same time (the library's streams and events are
+    shared under one lock): each thread's idx, W and M equal the same steps
+    run alone, bit for bit."""
+    import threading
+
+    shapes = [(512, 2048, 3), (2048, 512, 2)]
+    f, mu, eta = 0.25, 0.95, 0.04
+    params = d.make_ns_params(ns_dtype=d.F16)
+    ks = [d.dion3_k_from_fraction(min(r, c), f) for r, c, _ in shapes]
+
+    def make(seed0):
+        A = _groups(shapes, "bf16", step=0, seed0=seed0)
+        idx = [torch.empty(b, k, dtype=torch.int32, device=DEV) for (_, _, b), k in zip(shapes, ks)]
+        return A, idx
+
+    def run(A, idx, seed0, stream, barrier=None):
+        with torch.cuda.stream(stream):
+            plan = d.StepPlan([g[0] for g in A], [g[1] for g in A], [g[2] for g in A], ks, idx, params)
+            if barrier is not None:
+                barrier.wait()
+            for step in range(3):
+                for gi, (r, c, b) in enumerate(shapes):
+                    A[gi][2].copy_(synth.gradient(r, c, b, dtype="bf16", device=DEV, group_seed=seed0 + gi,
+                                                  step=step + 1))
+                plan.step_deferred(eta, 0.0, mu, has_prev=step > 0)
+            stream.synchronize()
+
+    seeds = [140, 150]
+    ref = []
+    for sd in seeds:                                   # each caller alone
+        A, idx = make(sd)
+        run(A, idx, sd, torch.cuda.Stream())
+        ref.append(([bits(g[0]) for g in A], [bits(g[1]) for g in A], [i.cpu().numpy() for i in idx]))
+    got = [make(sd) for sd in seeds]
+    barrier = threading.Barrier(2)
+    errors = []
+
+    def worker(j):
+        try:
+            run(got[j][0], got[j][1], seeds[j], torch.cuda.Stream(), barrier)
+        except Exception as e:                         # reported below
+            errors.append(e)
+
+    th = [threading.Thread(target=worker, args=(j,)) for j in range(2)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for j in range(2):
+        A, idx = got[j]
+        for gi in range(len(shapes)):
+            assert np.array_equal(bits(A[gi][0]), ref[j][0][gi]), (j, gi)
+            assert np.array_equal(bits(A[gi][1]), ref[j][1][gi]), (j, gi)
+            assert np.array_equal(idx[gi].cpu().numpy(), ref[j][2][gi]), (j, gi)
