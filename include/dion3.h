@@ -21,7 +21,12 @@
  *     structs are host values read during the call.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call is
  *     asynchronous and stream-ordered, does no host synchronisation and no
- *     allocation, and is deterministic run to run.
+ *     allocation, and is deterministic run to run.  The exceptions are
+ *     stated at their declarations: the whole-step calls create the
+ *     library's own streams and events on a device's first step,
+ *     dion3_step_graph_create creates graphs, dion3_timing_enable creates
+ *     events, and dion3_release waits for and destroys what the library
+ *     created.
  *   - Return value: DION3_OK (0) or a negative status.  Arguments are
  *     validated before anything is launched; on an error nothing is written.
  *     DION3_ERR_HIP means a launch failed (hipGetLastError was not success).
