@@ -122,13 +122,18 @@ def test_14b_three_steps(d):
     print(f"14b f=1/4 three steps worst O error {worst:.2e}")
 
 
-def test_7b_deferred_matches_immediate(d):
-    """The benchmark's deferred-decay step at full 7B size (f = 1/4) against
-    the immediate step over two steps: indices and W bit for bit after each
-    step, M bit for bit once the pending decay is completed."""
-    groups = synth.shape_groups("7b")
-    ks = [d.dion3_k_from_fraction(min(r, c), 0.25) for r, c, _ in groups]
-    mu, eta = 0.95, 0.04
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,f,steps", [("7b", 0.25, 2), ("14b", 0.25, 3), ("7b", 0.5, 2), ("7b", 1.0, 1),
+                                          ("1b", 0.125, 2)])
+def test_deferred_matches_immediate_full(d, name, f, steps):
+    """The benchmark's deferred step (decay carried into the next momentum
+    pass, the update of row-selected groups fused into the last product) at
+    the full size of every shape set against the immediate step with the
+    separate update: indices and W bit for bit after each step, M bit for bit
+    once the pending decay is completed."""
+    groups = synth.shape_groups(name)
+    ks = [d.dion3_k_from_fraction(min(r, c), f) for r, c, _ in groups]
+    mu, eta = 0.95, 0.02 / math.sqrt(f)
     params = d.make_ns_params(ns_dtype=d.F16)
     sets = []
     for _ in range(2):
@@ -140,7 +145,7 @@ def test_7b_deferred_matches_immediate(d):
             ids.append(torch.empty(b, ks[gi], dtype=torch.int32, device=DEV))
         sets.append((Ws, Ms, Gs, ids, d.StepPlan(Ws, Ms, Gs, ks, ids, params)))
     (Wa, Ma, Ga, ia, pa), (Wb, Mb, Gb, ib, pb) = sets
-    for step in range(2):
+    for step in range(steps):
         if step:
             for gi, (r, c, b) in enumerate(groups):
                 Gn = synth.gradient(r, c, b, dtype="bf16", device=DEV, group_seed=gi, step=step)
@@ -151,11 +156,12 @@ def test_7b_deferred_matches_immediate(d):
         pb.step_deferred(eta, 0.0, mu, has_prev=step > 0)
         torch.cuda.synchronize()
         for gi in range(len(groups)):
-            assert torch.equal(ia[gi], ib[gi]), (step, gi)
-            assert torch.equal(Wa[gi].view(torch.int16), Wb[gi].view(torch.int16)), (step, gi)
+            assert torch.equal(ia[gi], ib[gi]), (name, f, step, gi)
+            assert torch.equal(Wa[gi].view(torch.int16), Wb[gi].view(torch.int16)), (name, f, step, gi)
     pb.flush_decay(mu)
     torch.cuda.synchronize()
     for gi in range(len(groups)):
-        assert torch.equal(Ma[gi].view(torch.int16), Mb[gi].view(torch.int16)), gi
+        assert torch.equal(Ma[gi].view(torch.int16), Mb[gi].view(torch.int16)), (name, f, gi)
     del sets, Wa, Ma, Ga, Wb, Mb, Gb, pa, pb
+    torch.cuda.empty_cache()
     torch.cuda.empty_cache()
