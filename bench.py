@@ -378,6 +378,44 @@ def run_microbench(d, synth, torch):
     return out
 
 
+def run_ns_ladder(d, synth, torch, groups, ks):
+    """Gram against standard Newton-Schulz (same coefficients, restart after
+    iteration 2 for Gram) on one class batch of the workload each: a
+    Frobenius-normalised fp16 input of the class's shape [nb][k][m], 2
+    warm-up and 5 timed calls of each; ms per call and the ratio."""
+    classes = {}
+    for (r, c, b), k in zip(groups, ks):
+        classes.setdefault((k, max(r, c)), 0)
+        classes[(k, max(r, c))] += b
+    params = d.make_ns_params(ns_dtype=d.F16)
+    out = []
+    for (k, m), nb in classes.items():
+        if k == m:
+            continue
+        X = synth.dense(k, m, nb, dtype="f16", device="cuda:0", seed=7, std=1.0 / math.sqrt(k * m))
+        O = torch.empty_like(X)
+        res = {}
+        for name, fn, wsb in (("standard", d.dion3_standard_ns, d.dion3_standard_ns_workspace_bytes),
+                              ("gram", d.dion3_gram_ns_gathered, d.dion3_gram_ns_gathered_workspace_bytes)):
+            ws = d.workspace(wsb(nb, k, m, d.F16), "cuda:0")
+            for _ in range(2):
+                fn(X, O, params, ws)
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            s.record()
+            for _ in range(5):
+                fn(X, O, params, ws)
+            e.record()
+            torch.cuda.synchronize()
+            res[name] = s.elapsed_time(e) / 5
+            del ws
+        out.append({"batch": nb, "k": k, "m": m, "standard_ms": round(res["standard"], 3),
+                    "gram_ms": round(res["gram"], 3), "speedup": round(res["standard"] / res["gram"], 2)})
+        del X, O
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -413,6 +451,7 @@ def main():
 
     ms, pct, table, groups, ks, eta = run_step_bench(d, synth, torch, args)
     micro = [] if args.no_microbench else run_microbench(d, synth, torch)
+    ladder = [] if args.no_microbench else run_ns_ladder(d, synth, torch, groups, ks)
     if micro:
         print("# microbench done", file=sys.stderr, flush=True)
 
@@ -450,6 +489,7 @@ def main():
         "roofline": roof,
         "kernels": table,
         "sym_gemm": micro,
+        "ns_ladder": ladder,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
