@@ -82,10 +82,12 @@ static bool make_plan(int ng, const dion3_group* g, const int* k, const dion3_ns
 struct SideCtx {
   hipStream_t side = nullptr;   // gathers + Newton-Schulz, every compute unit (non-blocking)
   hipStream_t mem = nullptr;    // overlapped HBM-bound passes, half the compute units (blocking)
+  hipStream_t mem_all = nullptr;  // the same passes on every unit, for small steps (non-blocking)
   std::vector<hipEvent_t> ev;
   unsigned gen = 0;             // set when the streams are created (step graphs check it)
 };
 constexpr int kMaxDevices = 64;
+constexpr double kMaskedOverlapBytes = 8e9;   // see run_step
 static std::mutex g_side_mu;
 static SideCtx g_side[kMaxDevices];
 static unsigned g_side_gen = 0;
@@ -129,6 +131,10 @@ static int side_ctx(size_t nev, SideCtx** out) {
     c.mem = nullptr;
     return DION3_ERR_HIP;
   }
+  if (!c.mem_all && hipStreamCreateWithFlags(&c.mem_all, hipStreamNonBlocking) != hipSuccess) {
+    c.mem_all = nullptr;
+    return DION3_ERR_HIP;
+  }
   while (c.ev.size() < nev) {
     hipEvent_t e;
     if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return DION3_ERR_HIP;
@@ -144,11 +150,11 @@ int release_step_resources() {
   int prev = -1;
   for (int d = 0; d < kMaxDevices; ++d) {
     SideCtx& c = g_side[d];
-    if (!c.side && !c.mem && c.ev.empty()) continue;
+    if (!c.side && !c.mem && !c.mem_all && c.ev.empty()) continue;
     if (prev < 0 && hipGetDevice(&prev) != hipSuccess) prev = -1;
     if (hipSetDevice(d) != hipSuccess) { st = DION3_ERR_HIP; continue; }
     // the streams' queued work completes before they are destroyed
-    for (hipStream_t* q : {&c.side, &c.mem}) {
+    for (hipStream_t* q : {&c.side, &c.mem, &c.mem_all}) {
       if (!*q) continue;
       if (hipStreamSynchronize(*q) != hipSuccess || hipStreamDestroy(*q) != hipSuccess) st = DION3_ERR_HIP;
       *q = nullptr;
@@ -213,7 +219,16 @@ static int run_step(int n_groups, const dion3_group* groups, void* const* W, voi
   SideCtx* ctx = nullptr;
   int st = side_ctx(3 * (size_t)nc + 3, &ctx);
   if (st) return st;
-  hipStream_t side = ctx->side, mem = ctx->mem;
+  // The overlapped passes keep half of the units only when they are large:
+  // then the products beside them keep the other half (7B set: 26 GB of
+  // momentum traffic beside the first class's products, 26.3 against 27.1 ms
+  // per step with every unit).  Small passes are better spread over every unit
+  // (1B set: 4.8 GB, 2.92 against 3.10 ms).
+  double overlapped = 0.0;          // momentum bytes of the classes after the first
+  for (int c = 1; c < nc; ++c)
+    for (int i : P.classes[c])
+      overlapped += 3.0 * (double)dtype_size(groups[i].dtype) * groups[i].rows * groups[i].cols * groups[i].batch;
+  hipStream_t side = ctx->side, mem = overlapped >= kMaskedOverlapBytes ? ctx->mem : ctx->mem_all;
   hipEvent_t* ev_sel = ctx->ev.data();          // class c selected
   hipEvent_t* ev_ns = ev_sel + nc;              // class c orthogonalised (side stream)
   hipEvent_t* ev_upd = ev_ns + nc;              // class c updated
