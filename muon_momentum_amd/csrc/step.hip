@@ -127,14 +127,8 @@ static int side_ctx(size_t nev, SideCtx** out) {
     }
     c.gen = ++g_side_gen;
   }
-  if (!c.mem && make_mem_stream(dev, &c.mem) != DION3_OK) {
-    c.mem = nullptr;
-    return DION3_ERR_HIP;
-  }
-  if (!c.mem_all && hipStreamCreateWithFlags(&c.mem_all, hipStreamNonBlocking) != hipSuccess) {
-    c.mem_all = nullptr;
-    return DION3_ERR_HIP;
-  }
+  // the overlap streams are created when a step first needs one (run_step):
+  // a process holds only the kind its steps use
   while (c.ev.size() < nev) {
     hipEvent_t e;
     if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return DION3_ERR_HIP;
@@ -228,7 +222,20 @@ static int run_step(int n_groups, const dion3_group* groups, void* const* W, voi
   for (int c = 1; c < nc; ++c)
     for (int i : P.classes[c])
       overlapped += 3.0 * (double)dtype_size(groups[i].dtype) * groups[i].rows * groups[i].cols * groups[i].batch;
-  hipStream_t side = ctx->side, mem = overlapped >= kMaskedOverlapBytes ? ctx->mem : ctx->mem_all;
+  const bool masked = overlapped >= kMaskedOverlapBytes;
+  if (nc > 1) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return DION3_ERR_HIP;
+    if (masked && !ctx->mem && make_mem_stream(dev, &ctx->mem) != DION3_OK) {
+      ctx->mem = nullptr;
+      return DION3_ERR_HIP;
+    }
+    if (!masked && !ctx->mem_all && hipStreamCreateWithFlags(&ctx->mem_all, hipStreamNonBlocking) != hipSuccess) {
+      ctx->mem_all = nullptr;
+      return DION3_ERR_HIP;
+    }
+  }
+  hipStream_t side = ctx->side, mem = masked ? ctx->mem : ctx->mem_all;
   hipEvent_t* ev_sel = ctx->ev.data();          // class c selected
   hipEvent_t* ev_ns = ev_sel + nc;              // class c orthogonalised (side stream)
   hipEvent_t* ev_upd = ev_ns + nc;              // class c updated
