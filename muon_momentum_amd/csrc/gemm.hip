@@ -82,6 +82,7 @@ struct KParams {
   int ntiles;          // tiles over the batch
   int tiles_per_wg;    // large-tile kernel: tiles run back to back by one work-group
   int reverse;         // batch visited from its last matrix
+  int same;            // symmetric kernels: B is A (same pointer, leading dimension and stride)
   // fused update (large-tile Q X with APPLY): see GemmArgs
   void* W; long long sW; int wlines; const int32_t* idx;
   float eta, u; int decay;
@@ -462,6 +463,7 @@ __device__ __forceinline__ uint4 xchg8(const uint4& v) {
 struct TileAddr {
   int4v ra, rb;      // buffer resources based at the tile's first A row / B row or column
   int m0, n0, bat, ti, tj;
+  int bo;            // byte offset of the B fragments in a stage buffer
 };
 
 constexpr int kEpiStores = 32;   // 16-byte stores per wave in a Q X tile epilogue
@@ -589,9 +591,16 @@ void gemm256_kernel(KParams p) {
     a.n0 = a.tj * BN;
     const T* A = (const T*)p.A + a.bat * p.sA + (long long)a.m0 * p.lda;
     const T* B = (const T*)p.B + a.bat * p.sB + (BT ? (long long)a.n0 : (long long)a.n0 * p.ldb);
+    // a diagonal tile of a product whose B is A needs one operand panel:
+    // its B fragments are read from the A half of each stage, and its B
+    // loads, still issued so that every stage counts the same loads, go to
+    // a resource of zero bytes (out of range: no memory access)
+    const bool one_panel = SYM && p.same && a.ti == a.tj;
+    a.bo = one_panel ? 0 : 16384;
     a.ra = make_rsrc(A, (long long)(p.M - a.m0) * p.lda * 2);
-    a.rb = make_rsrc(B, BT ? (long long)p.K * p.ldb * 2 - (long long)a.n0 * 2
-                           : (long long)(p.N - a.n0) * p.ldb * 2);
+    a.rb = make_rsrc(B, one_panel ? 0LL
+                        : BT ? (long long)p.K * p.ldb * 2 - (long long)a.n0 * 2
+                             : (long long)(p.N - a.n0) * p.ldb * 2);
   };
 
   // one DMA instruction x (0..3: operand A, 4..7: operand B) of the tile's
@@ -616,8 +625,8 @@ void gemm256_kernel(KParams p) {
     const unsigned buf = lds0 + (unsigned)(b * STAGE);
     f = lds_read16(buf + swz32(wm * WT + i * 32 + (lane & 31), 2 * st + (lane >> 5)));
   };
-  auto read_b = [&](uint4& f, int b, int st, int j) {
-    const unsigned buf = lds0 + (unsigned)(b * STAGE) + 16384;
+  auto read_b = [&](uint4& f, int b, int st, int j, int bo) {
+    const unsigned buf = lds0 + (unsigned)(b * STAGE) + (unsigned)bo;
     if (!BT) {
       f = lds_read16(buf + swz32(wn * WT + j * 32 + (lane & 31), 2 * st + (lane >> 5)));
     } else {
@@ -1067,7 +1076,7 @@ void gemm256_kernel(KParams p) {
 
   uint4 fa0[SUB], fb0[SUB], fa1[SUB], fb1[SUB];
 #pragma unroll
-  for (int i = 0; i < SUB; ++i) { read_a(fa0[i], 0, 0, i); read_b(fb0[i], 0, 0, i); }
+  for (int i = 0; i < SUB; ++i) { read_a(fa0[i], 0, 0, i); read_b(fb0[i], 0, 0, i, cur.bo); }
 
   // One stage = 2 k-steps x 4 groups of 4 MFMAs.  Group x of a step issues
   // one DMA instruction of the stage NBUF - 1 ahead (spread out so the vector
@@ -1096,6 +1105,8 @@ void gemm256_kernel(KParams p) {
     const int ib = bcur == 0 ? NBUF - 1 : bcur - 1;
     int4v ira = cur.ra, irb = cur.rb;
     if (to_next) { ira = nxt.ra; irb = nxt.rb; }
+    // B fragments of the next stage: the next tile's after a tile's last stage
+    const int bo_next = kt == KT - 1 ? nxt.bo : cur.bo;
     static_for<2 * SUB>([&](auto gxc) {
       constexpr int gx = decltype(gxc)::value;
       constexpr int st = gx / SUB, x = gx % SUB;     // k-step, MFMA row block
@@ -1115,7 +1126,7 @@ void gemm256_kernel(KParams p) {
       uint4 (&cbv)[SUB] = st == 0 ? fb0 : fb1;
       auto next_frag = [&](int h) {
         if (!rd) return;
-        if (x < 2) read_b(nb[2 * x + h], ns, nst, 2 * x + h);
+        if (x < 2) read_b(nb[2 * x + h], ns, nst, 2 * x + h, st == 0 ? cur.bo : bo_next);
         else read_a(na[2 * x - 4 + h], ns, nst, 2 * x - 4 + h);
       };
       auto mfma = [&](int jj) {
@@ -1199,7 +1210,7 @@ void gemm256_kernel(KParams p) {
       // the next tile's first fragments (after the last tile: an in-bounds
       // read of a buffer no load is writing, unused)
 #pragma unroll
-      for (int i = 0; i < SUB; ++i) { read_a(fa0[i], bcur, 0, i); read_b(fb0[i], bcur, 0, i); }
+      for (int i = 0; i < SUB; ++i) { read_a(fa0[i], bcur, 0, i); read_b(fb0[i], bcur, 0, i, nxt.bo); }
       if (j + 1 < nt) {
         cur = nxt;
         if (j + 2 < nt) tile_addr(id + (j + 2) * G, nxt);
@@ -1284,6 +1295,7 @@ static int launch_typed(const GemmArgs& a, hipStream_t s) {
   p.C = a.C; p.ldc = a.ldc; p.sC = a.sC;
   p.alpha = a.alpha; p.beta = a.beta; p.gamma = a.gamma;
   p.reverse = a.reverse;
+  p.same = OP != OP_GEMM && a.A == a.B && a.lda == a.ldb && (a.batch == 1 || a.sA == a.sB);
   p.W = a.W; p.sW = a.sW; p.wlines = a.wlines; p.idx = a.idx;
   p.eta = a.eta; p.u = a.u; p.decay = a.decay;
 
