@@ -15,11 +15,12 @@
 // selection pass and its gather have nothing to overlap and run on the
 // caller's stream over the whole chip, and so does the last class's update;
 // the momentum passes and gathers of the other classes and the updates of all
-// but the last run on a second library stream restricted to half of the
-// compute units (spread evenly over the XCDs), in the order momentum and
+// but the last run on a second library stream, in the order momentum and
 // gather of class c + 1, then update of class c, so that these HBM-bound
-// passes overlap the products of class c without taking every compute unit
-// from them.  Events order the streams: class c's Newton-Schulz waits for its
+// passes overlap the products of class c.  When those momentum passes are
+// large that stream is restricted to half of the compute units (spread evenly
+// over the XCDs), so that they do not take every unit from the products;
+// small ones run on every unit.  Events order the streams: class c's Newton-Schulz waits for its
 // gather, class c's update for its Newton-Schulz, a gather for the end of the
 // Newton-Schulz that last read its buffer, and the caller's stream ends the
 // call having waited for all library-stream work.  Every kernel computes
