@@ -300,12 +300,14 @@ size_t dion3_step_workspace_bytes(int n_groups, const dion3_group* groups, const
  * (one value for all groups).
  * Streams: the first class's momentum pass and gather and the last class's
  * update are enqueued on `stream`; the Newton-Schulz products run on a side
- * stream, and the other momentum passes, gathers and updates on a stream
- * limited to half of the compute units, so that they overlap another class's
- * products.
- * The library streams belong to the current device; the library creates them
- * (with an event pool) on the device's first step and keeps them until the
- * process ends.  Graph capture is not supported: a call on a capturing stream
+ * stream, and the other momentum passes, gathers and updates on a third
+ * stream, so that they overlap another class's products; that stream is
+ * limited to half of the compute units when those momentum passes move at
+ * least 8 GB, and uses every unit otherwise.
+ * The library streams belong to the current device; the library creates each
+ * (with an event pool) when a step on the device first needs it and keeps
+ * them until dion3_release or the end of the process.
+ * Graph capture is not supported: a call on a capturing stream
  * returns DION3_ERR_UNSUPPORTED and enqueues nothing (a query of the capture
  * state that fails, e.g. on the legacy null stream while another stream
  * captures, returns DION3_ERR_HIP).  Events order all three against `stream`: when the call
