@@ -6,12 +6,15 @@
 //         ring buffer 4 stages ahead, waited for 2 stages ahead (vmcnt 16);
 //   READ  16 `ds_read_b128` fragment reads per wave (64 KB per unit);
 //   MFMA  32 `v_mfma_f32_32x32x16_f16` per wave (128 x 128 per wave);
-// interleaved as in the kernel (MFMA, read, MFMA, read, MFMA, DMA, MFMA) and
-// ended by a barrier.  Each mode runs a subset, so the cycles per stage of
-// each resource alone can be set against the combination.  The operands come
-// either from one 4 MB panel pair read by every work-group (resident in each
-// XCD's L2 after the first touch) or from a 4 MB pair per work-group (HBM).
-// Results are discarded; every access stays inside the buffers below.
+// interleaved as in the kernel (MFMA, read, MFMA, read, MFMA, DMA, MFMA; the
+// loads of the steady state issued without a test) and ended by a barrier.
+// Each mode runs a subset, so the cycles per stage of each resource alone can
+// be set against the combination, and the clock (shader cycles over wall
+// time) shows what the MFMAs cost in power: the operands are random finite
+// fp16 values or zeros, and come either from one 4 MB panel pair read by
+// every work-group (resident in each XCD's L2 after the first touch) or from
+// a 4 MB pair per work-group (HBM).  Results are discarded; every access
+// stays inside the buffers below.
 //
 //   hipcc --offload-arch=gfx950 -O3 -std=c++17 \
 //     -Xclang -target-feature -Xclang -packed-fp32-ops \
@@ -19,6 +22,7 @@
 #include <hip/hip_runtime.h>
 #include <cstdio>
 #include <cstdlib>
+#include <type_traits>
 #include <vector>
 
 typedef int int4v __attribute__((ext_vector_type(4)));
@@ -51,6 +55,13 @@ __device__ __forceinline__ void lds_dma16(const int4v& rsrc, unsigned lds, int v
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :: "s"(m0), "v"(voffset), "s"(rsrc), "s"(soffset) : "memory", "m0");
 }
+// two finite fp16 values of magnitude below 2 from a hash of k
+__host__ __device__ __forceinline__ unsigned mix(unsigned x) {
+  x ^= x >> 13;
+  x *= 0x5bd1e995u;
+  x ^= x >> 15;
+  return x & 0xbbffbbffu;
+}
 __device__ __forceinline__ int swz32(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); }
 __device__ __forceinline__ u32x4v lds_read16(unsigned addr) {
   return *(const __attribute__((address_space(3))) u32x4v*)(uintptr_t)addr;
@@ -60,7 +71,7 @@ constexpr int kDma = 1, kRead = 2, kMfma = 4;
 
 template <int MODE>
 __global__ __launch_bounds__(256, 1) void stage_probe(const char* src, long long wg_stride, int ld_bytes, int S,
-                                                      unsigned long long* cyc, float* sink) {
+                                                      bool random, unsigned long long* cyc, float* sink) {
   constexpr bool DMA = MODE & kDma, RD = MODE & kRead, MF = MODE & kMfma;
   __shared__ __attribute__((aligned(1024))) char smem[5 * 32768];
   const unsigned lds0 = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)smem;
@@ -83,8 +94,14 @@ __global__ __launch_bounds__(256, 1) void stage_probe(const char* src, long long
   for (int i = 0; i < 4; ++i)
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
   u32x4v fa[2][4], fb[2][4];
+  // fragments for the modes without LDS reads: the same kind of values
+  auto rnd = [&](unsigned k) { return mix(k * 2654435761u + threadIdx.x * 40503u + 12345u); };
   for (int h = 0; h < 2; ++h)
-    for (int i = 0; i < 4; ++i) { fa[h][i] = u32x4v{1, 2, 3, 4}; fb[h][i] = fa[h][i]; }
+    for (int i = 0; i < 4; ++i)
+      for (int e = 0; e < 4; ++e) {
+        fa[h][i][e] = random ? rnd(16 * h + 4 * i + e) : 0u;
+        fb[h][i][e] = random ? rnd(100 + 16 * h + 4 * i + e) : 0u;
+      }
   const unsigned long long t0 = __builtin_readcyclecounter();
   if (DMA) {
     for (int g = 0; g < 4 && g < S; ++g)
@@ -93,9 +110,12 @@ __global__ __launch_bounds__(256, 1) void stage_probe(const char* src, long long
   }
   __syncthreads();
   int bcur = 0;
-  for (int g = 0; g < S; ++g) {
+  int g = 0;
+  // one stage; ISS: the stage 4 ahead exists (its loads are issued without a
+  // test, as in the kernel's steady state)
+  auto stage = [&](auto iss_c) {
+    constexpr bool ISS = decltype(iss_c)::value;
     const int ib = bcur == 0 ? 4 : bcur - 1;          // buffer of stage g + 4
-    const bool iss = DMA && g + 4 < S;
 #pragma unroll
     for (int gx = 0; gx < 8; ++gx) {
       const int st = gx / 4, x = gx % 4;
@@ -127,18 +147,21 @@ __global__ __launch_bounds__(256, 1) void stage_probe(const char* src, long long
       __builtin_amdgcn_sched_barrier(0);
       mm(2);
       __builtin_amdgcn_sched_barrier(0);
-      if (iss) dma(g + 4, ib, gx);
+      if (DMA && ISS) dma(g + 4, ib, gx);
       __builtin_amdgcn_sched_barrier(0);
       mm(3);
     }
     __builtin_amdgcn_sched_barrier(0);
     if (DMA) {
-      if (g + 4 < S) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");   // stage g + 2 landed
+      if (ISS) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");   // stage g + 2 landed
       else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     asm volatile("s_barrier" ::: "memory");
     bcur = bcur == 4 ? 0 : bcur + 1;
-  }
+    ++g;
+  };
+  for (int t = 0; t < S - 4; ++t) stage(std::true_type{});
+  for (int t = S - 4; t < S; ++t) stage(std::false_type{});
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __syncthreads();
   const unsigned long long t1 = __builtin_readcyclecounter();
@@ -151,19 +174,24 @@ __global__ __launch_bounds__(256, 1) void stage_probe(const char* src, long long
   if (threadIdx.x == 0) cyc[blockIdx.x] = t1 - t0;
 }
 
+__global__ void fill_random(unsigned* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+    p[i] = mix((unsigned)i * 2654435761u + 777u);
+}
+
 template <int MODE>
 static void run(const char* name, const char* src, long long wg_stride, int ld_bytes, int S, int grid,
-                unsigned long long* cyc, float* sink) {
+                bool random, unsigned long long* cyc, float* sink) {
   hipEvent_t e0, e1;
   CHECK(hipEventCreate(&e0));
   CHECK(hipEventCreate(&e1));
-  stage_probe<MODE><<<grid, 256>>>(src, wg_stride, ld_bytes, S, cyc, sink);
+  stage_probe<MODE><<<grid, 256>>>(src, wg_stride, ld_bytes, S, random, cyc, sink);
   CHECK(hipGetLastError());
   CHECK(hipDeviceSynchronize());
   float best = 1e9f;
   for (int r = 0; r < 5; ++r) {
     CHECK(hipEventRecord(e0));
-    stage_probe<MODE><<<grid, 256>>>(src, wg_stride, ld_bytes, S, cyc, sink);
+    stage_probe<MODE><<<grid, 256>>>(src, wg_stride, ld_bytes, S, random, cyc, sink);
     CHECK(hipEventRecord(e1));
     CHECK(hipEventSynchronize(e1));
     float ms = 0.f;
@@ -191,23 +219,32 @@ int main() {
   const int maxg = 256;
   char* src = nullptr;
   CHECK(hipMalloc(&src, pair * maxg));
-  CHECK(hipMemset(src, 0, pair * maxg));
   unsigned long long* cyc = nullptr;
   CHECK(hipMalloc(&cyc, maxg * sizeof(unsigned long long)));
   float* sink = nullptr;
   CHECK(hipMalloc(&sink, sizeof(float)));
-  for (int shared = 1; shared >= 0; --shared) {
-    printf("# operands: %s\n", shared ? "one 4 MB panel pair read by every work-group (L2-resident)"
-                                      : "a 4 MB panel pair per work-group (HBM)");
-    const long long stride = shared ? 0 : pair;
-    for (int grid : {256, 176}) {
-      run<kDma>("dma", src, stride, ld, S, grid, cyc, sink);
-      run<kRead>("read", src, stride, ld, S, grid, cyc, sink);
-      run<kMfma>("mfma", src, stride, ld, S, grid, cyc, sink);
-      run<kDma | kRead>("dma+read", src, stride, ld, S, grid, cyc, sink);
-      run<kDma | kMfma>("dma+mfma", src, stride, ld, S, grid, cyc, sink);
-      run<kRead | kMfma>("read+mfma", src, stride, ld, S, grid, cyc, sink);
-      run<kDma | kRead | kMfma>("all", src, stride, ld, S, grid, cyc, sink);
+  for (int random = 1; random >= 0; --random) {
+    if (random) {
+      fill_random<<<4096, 256>>>((unsigned*)src, (size_t)(pair * maxg / 4));
+      CHECK(hipGetLastError());
+    } else {
+      CHECK(hipMemset(src, 0, pair * maxg));
+    }
+    CHECK(hipDeviceSynchronize());
+    for (int shared = 1; shared >= 0; --shared) {
+      printf("# %s operands: %s\n", random ? "random fp16" : "zero",
+             shared ? "one 4 MB panel pair read by every work-group (L2-resident)"
+                    : "a 4 MB panel pair per work-group (HBM)");
+      const long long stride = shared ? 0 : pair;
+      for (int grid : {256, 176}) {
+        if (!shared && grid != 256) continue;
+        run<kMfma>("mfma", src, stride, ld, S, grid, random, cyc, sink);
+        run<kRead | kMfma>("read+mfma", src, stride, ld, S, grid, random, cyc, sink);
+        run<kDma>("dma", src, stride, ld, S, grid, random, cyc, sink);
+        run<kDma | kRead>("dma+read", src, stride, ld, S, grid, random, cyc, sink);
+        run<kDma | kMfma>("dma+mfma", src, stride, ld, S, grid, random, cyc, sink);
+        run<kDma | kRead | kMfma>("all", src, stride, ld, S, grid, random, cyc, sink);
+      }
     }
   }
   CHECK(hipFree(src));
