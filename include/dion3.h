@@ -23,10 +23,10 @@
  *     asynchronous and stream-ordered, does no host synchronisation and no
  *     allocation, and is deterministic run to run.  The exceptions are
  *     stated at their declarations: the whole-step calls create the
- *     library's own streams and events on a device's first step,
- *     dion3_step_graph_create creates graphs, dion3_timing_enable creates
- *     events, and dion3_release waits for and destroys what the library
- *     created.
+ *     library's own streams and events when a step on a device first needs
+ *     them, dion3_step_graph_create creates graphs, dion3_timing_enable
+ *     creates events, dion3_timing_report waits for the recorded events, and
+ *     dion3_release waits for and destroys what the library created.
  *   - Return value: DION3_OK (0) or a negative status.  Arguments are
  *     validated before anything is launched; on an error nothing is written.
  *     DION3_ERR_HIP means a launch failed (hipGetLastError was not success).
@@ -399,11 +399,12 @@ int dion3_release(void);
 
 /* Per-kernel timing with hipEvents, for benchmarks.  dion3_timing_enable(n)
  * creates a pool of n event pairs (n = 0 disables and frees it); while enabled
- * every launch of the library records an event pair on its stream.  This is
- * the only call that allocates.  dion3_timing_report writes one line per
- * kernel name, "name count total_ms\n", into buf (synchronising on the
+ * every launch of the library records an event pair on its stream (none
+ * while a step graph is being built).  dion3_timing_report writes one line
+ * per kernel name, "name count total_ms\n", into buf (synchronising on the
  * recorded events) and clears the pool.  Returns the bytes written or a
- * negative status. */
+ * negative status.  The pool is process-wide and unsynchronised: enable
+ * timing only while one thread issues library calls. */
 int dion3_timing_enable(int max_launches);
 int dion3_timing_report(char* buf, size_t buf_bytes);
 
