@@ -298,6 +298,8 @@ size_t dion3_step_workspace_bytes(int n_groups, const dion3_group* groups, const
  * dion3_apply_rows.  W[i], M[i], G[i] are the group tensors, idx[i] receives
  * the [batch][k[i]] selected indices.  eta, wd, mu as in dion3_apply_rows
  * (one value for all groups).
+ * The (k, m) classes are processed in order of increasing momentum traffic
+ * (bytes of M of their groups), whatever the order of the groups.
  * Streams: the first class's momentum pass and gather and the last class's
  * update are enqueued on `stream`; the Newton-Schulz products run on a side
  * stream, and the other momentum passes, gathers and updates on a third

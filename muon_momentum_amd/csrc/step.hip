@@ -26,6 +26,7 @@
 // call having waited for all library-stream work.  Every kernel computes
 // exactly what it computes on one stream, so the results do not depend on
 // the overlap.
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -36,7 +37,7 @@ static inline size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Plan {
   std::vector<int> n, m, axis;
-  std::vector<std::vector<int>> classes;   // groups sharing (k, m), in order of first appearance
+  std::vector<std::vector<int>> classes;   // groups sharing (k, m), by increasing momentum traffic
   std::vector<size_t> sqn_off;             // per group: offset of its [batch] fp64 slot
   std::vector<size_t> rs_off;              // per group: offset of its [batch][k] fp32 row factors
   size_t rowsel = 0, sqn = 0, rs = 0, xbuf = 0, gram = 0;
@@ -64,6 +65,17 @@ static bool make_plan(int ng, const dion3_group* g, const int* k, const dion3_ns
       if (k[c[0]] == k[i] && P.m[c[0]] == P.m[i]) { c.push_back(i); placed = true; break; }
     if (!placed) P.classes.push_back({i});
   }
+  // the first class's momentum pass has nothing beside it and the last
+  // class's products have no momentum pass beside them: the class with the
+  // least momentum traffic goes first (7B set: 26.0 against 27.0 ms per step
+  // with the larger class first), whatever the order of the groups
+  auto traffic = [&](const std::vector<int>& c) {
+    double t = 0.0;
+    for (int i : c) t += (double)dtype_size(g[i].dtype) * g[i].rows * g[i].cols * g[i].batch;
+    return t;
+  };
+  std::stable_sort(P.classes.begin(), P.classes.end(),
+                   [&](const std::vector<int>& a, const std::vector<int>& b) { return traffic(a) < traffic(b); });
   for (auto& c : P.classes) {
     int nb = 0;
     for (int i : c) nb += g[i].batch;
