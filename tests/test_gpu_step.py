@@ -105,6 +105,10 @@ def test_multigroup_bf16_step_matches_manual_and_oracle(d, f):
     [(128, 512, 3)],                                 # a single class
     [(200, 96, 1), (128, 512, 1), (512, 128, 1)],    # single matrices, two of them in one class
     [(64, 256, 2), (128, 256, 1), (96, 320, 2), (256, 256, 1), (64, 512, 3)],   # five classes
+    # the step takes classes in order of increasing momentum traffic: these
+    # groups arrive in another order
+    [(128, 512, 3), (512, 128, 2), (256, 256, 1)],
+    [(64, 512, 3), (256, 256, 1), (96, 320, 2), (128, 256, 1), (64, 256, 2)],
 ])
 def test_step_class_layouts_match_manual(d, shapes):
     """Classes made of several groups, a single class, classes of single
