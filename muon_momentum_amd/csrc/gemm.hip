@@ -595,8 +595,11 @@ void gemm256_kernel(KParams p) {
     // its B fragments are read from the A half of each stage, and its B
     // loads, still issued so that every stage counts the same loads, go to
     // a resource of zero bytes (out of range: no memory access)
+    // (the wave of the quadrant above the diagonal, whose results are never
+    // stored, reads the B half instead: the out-of-range loads leave zeros
+    // there, and MFMAs on zeros draw less power)
     const bool one_panel = SYM && p.same && a.ti == a.tj;
-    a.bo = one_panel ? 0 : 16384;
+    a.bo = one_panel && wm >= wn ? 0 : 16384;
     a.ra = make_rsrc(A, (long long)(p.M - a.m0) * p.lda * 2);
     a.rb = make_rsrc(B, one_panel ? 0LL
                         : BT ? (long long)p.K * p.ldb * 2 - (long long)a.n0 * 2
