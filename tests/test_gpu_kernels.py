@@ -473,6 +473,40 @@ def test_products_independent_of_batch(d):
     assert torch.equal(Y[3].view(torch.int16), Y1[0].view(torch.int16)), "gemm"
 
 
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_multi_tile_products_match_single_matrices(d, dt):
+    """Batches large enough for work-groups that run several 256 x 256 tiles
+    back to back (diagonal and off-diagonal tiles of different matrices in
+    one work-group, one-panel diagonal tiles of X X^T and A^2 + B among them)
+    against every matrix computed alone, where the 128 x 128 kernel runs it:
+    the same bits for every matrix."""
+    g = torch.Generator(device="cpu").manual_seed(19)
+    t = TD[dt]
+    n, m, b = 1024, 2048, 48
+    X = (torch.randn(b, n, m, generator=g) / m ** 0.5).to(t).to(DEV)
+    A = (torch.randn(b, n, n, generator=g) / n ** 0.5)
+    A = ((A + A.transpose(1, 2)) * 0.5).to(t).to(DEV).contiguous()
+    B = (torch.randn(b, n, n, generator=g) / n ** 0.5)
+    B = ((B + B.transpose(1, 2)) * 0.5).to(t).to(DEV).contiguous()
+    one = torch.empty(1, n, n, dtype=t, device=DEV)
+    onex = torch.empty(1, n, m, dtype=t, device=DEV)
+    cases = [
+        ("syrk", lambda out, sl: d.dion3_syrk(X[sl], out, 1.0, 0.0), (n, n)),
+        ("sym_sq_add", lambda out, sl: d.dion3_sym_sq_add(A[sl], B[sl], out, 0.5, -1.25, 2.0), (n, n)),
+        ("sym_mul", lambda out, sl: d.dion3_sym_mul(A[sl], B[sl], out, 1.0), (n, n)),
+        ("gemm", lambda out, sl: d.dion3_gemm(A[sl], X[sl], out, 1.0), (n, m)),
+    ]
+    for name, run, shape in cases:
+        full = torch.empty(b, *shape, dtype=t, device=DEV)
+        run(full, slice(0, b))
+        torch.cuda.synchronize()
+        for i in range(b):
+            single = one if shape == (n, n) else onex
+            run(single, slice(i, i + 1))
+            torch.cuda.synchronize()
+            assert torch.equal(full[i].view(torch.int16), single[0].view(torch.int16)), (name, i)
+
+
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
 def test_count_nonfinite(d, dt):
     """dion3_count_nonfinite counts NaN and +-Inf entries exactly: planted at
