@@ -4,6 +4,9 @@
 // work-group per compute unit (the stage ring takes the whole 160 KB of LDS):
 //   DMA   8 `buffer_load_dwordx4 ... lds` per wave: 32 KB of operands into the
 //         ring buffer 4 stages ahead, waited for 2 stages ahead (vmcnt 16);
+//         either as the kernel loads them (16 rows x 64 bytes per instruction)
+//         or as whole 128-byte lines (8 rows x 128 bytes: a layout with two
+//         stages' K per row);
 //   READ  16 `ds_read_b128` fragment reads per wave (64 KB per unit);
 //   MFMA  32 `v_mfma_f32_32x32x16_f16` per wave (128 x 128 per wave);
 // interleaved as in the kernel (MFMA, read, MFMA, read, MFMA, DMA, MFMA; the
@@ -67,12 +70,12 @@ __device__ __forceinline__ u32x4v lds_read16(unsigned addr) {
   return *(const __attribute__((address_space(3))) u32x4v*)(uintptr_t)addr;
 }
 
-constexpr int kDma = 1, kRead = 2, kMfma = 4;
+constexpr int kDma = 1, kRead = 2, kMfma = 4, kWide = 8;
 
 template <int MODE>
 __global__ __launch_bounds__(256, 1) void stage_probe(const char* src, long long wg_stride, int ld_bytes, int S,
                                                       bool random, unsigned long long* cyc, float* sink) {
-  constexpr bool DMA = MODE & kDma, RD = MODE & kRead, MF = MODE & kMfma;
+  constexpr bool DMA = MODE & kDma, RD = MODE & kRead, MF = MODE & kMfma, WIDE = MODE & kWide;
   __shared__ __attribute__((aligned(1024))) char smem[5 * 32768];
   const unsigned lds0 = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)smem;
   const int lane = threadIdx.x & 63;
@@ -82,13 +85,24 @@ __global__ __launch_bounds__(256, 1) void stage_probe(const char* src, long long
   // A: rows 0..255 of the pair, B: rows 256..511; ld_bytes per row, S stages of 64 bytes
   const int4v ra = make_rsrc(base, 256LL * ld_bytes);
   const int4v rb = make_rsrc(base + 256LL * ld_bytes, 256LL * ld_bytes);
-  const int va = (16 * wave + (lane >> 2)) * ld_bytes + (((lane & 3) ^ (lane >> 4)) << 4);
-  const int ka = 64 * ld_bytes;
+  // narrow (the kernel's layout): an instruction covers 16 rows x 64 bytes,
+  // half of each 128-byte line.  WIDE: 8 rows x 128 bytes, whole lines, as a
+  // layout holding two stages' K per row would load them (stage s: rows
+  // 128 (s mod 2) .. + 127 of each operand, bytes 128 (s / 2) .. + 127)
+  const int va = WIDE ? (8 * wave + (lane >> 3)) * ld_bytes + ((lane & 7) << 4)
+                      : (16 * wave + (lane >> 2)) * ld_bytes + (((lane & 3) ^ (lane >> 4)) << 4);
+  const int ka = (WIDE ? 32 : 64) * ld_bytes;
   auto dma = [&](int ls, int b, int x) {
     const unsigned buf = lds0 + (unsigned)(b * 32768);
     const int q = x & 3;
-    if (x < 4) lds_dma16(ra, buf + (64 * q + 16 * wave) * 64, va, ls * 64 + q * ka);
-    else lds_dma16(rb, buf + 16384 + (64 * q + 16 * wave) * 64, va, ls * 64 + q * ka);
+    if (WIDE) {
+      const int off = (ls & 1) * 128 * ld_bytes + (ls >> 1) * 128 + q * ka;
+      if (x < 4) lds_dma16(ra, buf + (32 * q + 8 * wave) * 128, va, off);
+      else lds_dma16(rb, buf + 16384 + (32 * q + 8 * wave) * 128, va, off);
+    } else {
+      if (x < 4) lds_dma16(ra, buf + (64 * q + 16 * wave) * 64, va, ls * 64 + q * ka);
+      else lds_dma16(rb, buf + 16384 + (64 * q + 16 * wave) * 64, va, ls * 64 + q * ka);
+    }
   };
   floatx16 acc[4][4];
   for (int i = 0; i < 4; ++i)
@@ -244,6 +258,11 @@ int main() {
         run<kDma | kRead>("dma+read", src, stride, ld, S, grid, random, cyc, sink);
         run<kDma | kMfma>("dma+mfma", src, stride, ld, S, grid, random, cyc, sink);
         run<kDma | kRead | kMfma>("all", src, stride, ld, S, grid, random, cyc, sink);
+        if (shared && grid == 256) {
+          run<kDma | kWide>("dma-wide", src, stride, ld, S, grid, random, cyc, sink);
+          run<kDma | kMfma | kWide>("wide+mfma", src, stride, ld, S, grid, random, cyc, sink);
+          run<kDma | kRead | kMfma | kWide>("wide+all", src, stride, ld, S, grid, random, cyc, sink);
+        }
       }
     }
   }
