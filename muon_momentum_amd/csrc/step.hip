@@ -87,8 +87,9 @@ static bool make_plan(int ng, const dion3_group* g, const int* k, const dion3_ns
   return true;
 }
 
-// The library streams (default priority) and an event pool, created on a
-// device's first step and kept until the process ends.  Enqueueing a step
+// The library streams (default priority) and an event pool, each created
+// when a step on the device first needs it and kept until dion3_release or
+// the end of the process.  Enqueueing a step
 // holds the mutex, so concurrent callers do not interleave their use of the
 // events.  The compute-unit-masked stream is a blocking stream (its creation
 // call takes no flags, so it synchronises with the legacy null stream).
