@@ -118,3 +118,37 @@ def test_7b_momentum_bytes(bench):
     ks = [math.ceil(min(r, c) / 4) for r, c, _ in groups]
     work = bench.kernel_work(groups, ks)
     assert work["momentum_keys"] == ("hbm", 6 * params)
+
+
+def test_traffic_lookup_follows_the_source(bench, tmp_path, monkeypatch):
+    """bench.py reports a kernel's counter-measured HBM bytes only while the
+    kernel's source (and common.h) hash equals the one recorded beside the
+    counters, and only for the workload they were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("rowsel.hip", "common.h"):
+        with open(os.path.join(ROOT, "muon_momentum_amd", "csrc", name), "rb") as fh:
+            h.update(fh.read())
+    good = h.hexdigest()[:16]
+    f = tmp_path / "traffic.txt"
+    f.write_text("# header\n"
+                 f"traffic kernel=momentum_keys launches=2 fetch_bytes=1e9 write_bytes=5e8 total_bytes=1.5e9 "
+                 f"source=rowsel.hip src_sha256={good}\n"
+                 "traffic kernel=topk_select launches=2 fetch_bytes=1 write_bytes=1 total_bytes=2 "
+                 "source=rowsel.hip src_sha256=0000000000000000\n")
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.measured_traffic("momentum_keys", "7b", 0.25) == 1.5e9
+    assert bench.measured_traffic("topk_select", "7b", 0.25) is None        # stale hash
+    assert bench.measured_traffic("momentum_keys", "1b", 0.125) is None     # another workload
+    assert bench.measured_traffic("gemm_qx", "7b", 0.25) is None            # no line
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark has no multi-GPU path: --gpus above 1 exits with a
+    message, before touching a GPU."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
