@@ -275,13 +275,17 @@ def run_step_bench(d, synth, torch, args):
            "p90": per_step[min(len(per_step) - 1, int(math.ceil(0.9 * len(per_step))) - 1)]}
     print(f"# timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
 
-    # the same step as HIP graphs (dion3_step_graph_create): per-stream
+    # the same step as HIP graphs (dion3_step_graph_create, or
+    # dion3_step_normuon_graph_create for the NorMuon flavour): per-stream
     # segments replayed on the library's streams ("graph"), and one graph of
     # the whole step ("graph_one"); enqueue time of one launch and K launches
     # timed as above
-    if args.flavor == "muon" and not args.no_graph:
+    if not args.no_graph:
         for key, one in (("graph", False), ("graph_one", True)):
-            graph = plan.graph(eta, 0.0, MU, has_prev=True, one=one)
+            if args.flavor == "normuon":
+                graph = plan.graph_normuon(Vs, eta, 0.0, MU, has_prev=True, one=one)
+            else:
+                graph = plan.graph(eta, 0.0, MU, has_prev=True, one=one)
             for _ in range(3):
                 graph.launch()
             ghost = []

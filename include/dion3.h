@@ -386,6 +386,17 @@ int dion3_step_normuon(int n_groups, const dion3_group* groups, void* const* W, 
                        int deferred, int has_prev, const dion3_ns_params* p, float eta, float wd,
                        float mu, float beta2, float nm_eps, void* ws, size_t ws_bytes, void* stream);
 
+/* The deferred NorMuon step (dion3_step_normuon with deferred = 1) as HIP
+ * graphs: built, launched (dion3_graph_launch) and destroyed
+ * (dion3_graph_destroy) exactly as dion3_step_graph_create's, with V, beta2
+ * and nm_eps as in dion3_step_normuon; a launch performs that step on the
+ * buffers' current contents, bit-identical to the eager call. */
+int dion3_step_normuon_graph_create(int n_groups, const dion3_group* groups, void* const* W, void* const* M,
+                                    const void* const* G, const int* k, int32_t* const* idx, float* const* V,
+                                    int has_prev, const dion3_ns_params* p, float eta, float wd, float mu,
+                                    float beta2, float nm_eps, void* ws, size_t ws_bytes, unsigned flags,
+                                    dion3_graph* out);
+
 /* ------------------------------------------------------------- teardown */
 
 /* Destroys what the library created by itself: the whole-step streams and

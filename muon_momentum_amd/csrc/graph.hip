@@ -171,21 +171,10 @@ static void destroy_segments(std::vector<GraphSegment>& segs, int* st) {
   }
 }
 
-extern "C" int dion3_step_graph_create(int n_groups, const dion3_group* groups, void* const* W,
-                                       void* const* M, const void* const* G, const int* k,
-                                       int32_t* const* idx, int has_prev, const dion3_ns_params* p,
-                                       float eta, float wd, float mu, void* ws, size_t ws_bytes,
-                                       unsigned flags, dion3_graph* out) {
-  if (!out) return DION3_ERR_INVALID_ARG;
-  *out = nullptr;
-  if (flags & ~(unsigned)DION3_GRAPH_ONE) return DION3_ERR_INVALID_ARG;
-  // the step's own checks, before any HIP call
-  if (!W || !M || !G || !idx || !k || n_groups < 1) return DION3_ERR_INVALID_ARG;
-  for (int i = 0; i < n_groups; ++i)
-    if (!W[i] || !M[i] || !G[i] || !idx[i]) return DION3_ERR_INVALID_ARG;
-  const size_t need = dion3_step_workspace_bytes(n_groups, groups, k, p);
-  if (!need) return DION3_ERR_INVALID_ARG;
-  if (!ws || ws_bytes < need) return DION3_ERR_WORKSPACE;
+// Builds the graphs of one step: `run` enqueues the step (the driver, with
+// this thread's builder active).
+template <typename Run>
+static int build_step_graph(unsigned flags, dion3_graph* out, Run run) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return DION3_ERR_HIP;
   GraphBuilder b;
@@ -197,8 +186,7 @@ extern "C" int dion3_step_graph_create(int n_groups, const dion3_group* groups, 
     b.segs.push_back(g);
   }
   t_builder = &b;
-  int st = run_step_deferred(n_groups, groups, W, M, G, k, idx, has_prev, p, eta, wd, mu, ws, ws_bytes,
-                             nullptr);
+  int st = run();
   t_builder = nullptr;
   b.close_all();
   if (!st) st = b.status;
@@ -227,6 +215,52 @@ extern "C" int dion3_step_graph_create(int n_groups, const dion3_group* groups, 
   g->gen = gen;
   *out = g;
   return DION3_OK;
+}
+
+// The step's own argument checks that need no HIP call.
+static int check_step_args(int n_groups, const dion3_group* groups, void* const* W, void* const* M,
+                           const void* const* G, const int* k, int32_t* const* idx, const dion3_ns_params* p,
+                           void* ws, size_t ws_bytes) {
+  if (!W || !M || !G || !idx || !k || n_groups < 1) return DION3_ERR_INVALID_ARG;
+  for (int i = 0; i < n_groups; ++i)
+    if (!W[i] || !M[i] || !G[i] || !idx[i]) return DION3_ERR_INVALID_ARG;
+  const size_t need = dion3_step_workspace_bytes(n_groups, groups, k, p);
+  if (!need) return DION3_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < need) return DION3_ERR_WORKSPACE;
+  return DION3_OK;
+}
+
+extern "C" int dion3_step_graph_create(int n_groups, const dion3_group* groups, void* const* W,
+                                       void* const* M, const void* const* G, const int* k,
+                                       int32_t* const* idx, int has_prev, const dion3_ns_params* p,
+                                       float eta, float wd, float mu, void* ws, size_t ws_bytes,
+                                       unsigned flags, dion3_graph* out) {
+  if (!out) return DION3_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (flags & ~(unsigned)DION3_GRAPH_ONE) return DION3_ERR_INVALID_ARG;
+  if (int st = check_step_args(n_groups, groups, W, M, G, k, idx, p, ws, ws_bytes)) return st;
+  return build_step_graph(flags, out, [&] {
+    return run_step_deferred(n_groups, groups, W, M, G, k, idx, has_prev, p, eta, wd, mu, ws, ws_bytes, nullptr);
+  });
+}
+
+extern "C" int dion3_step_normuon_graph_create(int n_groups, const dion3_group* groups, void* const* W,
+                                               void* const* M, const void* const* G, const int* k,
+                                               int32_t* const* idx, float* const* V, int has_prev,
+                                               const dion3_ns_params* p, float eta, float wd, float mu,
+                                               float beta2, float nm_eps, void* ws, size_t ws_bytes,
+                                               unsigned flags, dion3_graph* out) {
+  if (!out) return DION3_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (flags & ~(unsigned)DION3_GRAPH_ONE) return DION3_ERR_INVALID_ARG;
+  if (!V) return DION3_ERR_INVALID_ARG;
+  for (int i = 0; i < n_groups && V; ++i)
+    if (!V[i]) return DION3_ERR_INVALID_ARG;
+  if (int st = check_step_args(n_groups, groups, W, M, G, k, idx, p, ws, ws_bytes)) return st;
+  return build_step_graph(flags, out, [&] {
+    return dion3_step_normuon(n_groups, groups, W, M, G, k, idx, V, 1, has_prev, p, eta, wd, mu, beta2, nm_eps,
+                              ws, ws_bytes, nullptr);
+  });
 }
 
 extern "C" int dion3_graph_launch(dion3_graph g, void* stream) {

@@ -92,6 +92,10 @@ def _load() -> ctypes.CDLL:
         "dion3_step_graph_create": (i, [i, gp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
                                         ctypes.POINTER(i), ctypes.POINTER(vp), i, pp, f, f, f, vp, sz,
                                         ctypes.c_uint, ctypes.POINTER(vp)]),
+        "dion3_step_normuon_graph_create": (i, [i, gp, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                                ctypes.POINTER(vp), ctypes.POINTER(i), ctypes.POINTER(vp),
+                                                ctypes.POINTER(vp), i, pp, f, f, f, f, f, vp, sz,
+                                                ctypes.c_uint, ctypes.POINTER(vp)]),
         "dion3_graph_launch": (i, [vp, vp]),
         "dion3_count_nonfinite": (i, [vp, i, sz, vp, vp]),
         "dion3_graph_destroy": (i, [vp]),
@@ -371,6 +375,18 @@ class StepPlan:
                                            ctypes.byref(g)),
                "dion3_step_graph_create")
         return StepGraph(g, self)
+
+    def graph_normuon(self, Vs, eta, wd, mu, beta2=0.95, nm_eps=1e-8, has_prev=True, one=False):
+        """dion3_step_normuon_graph_create: the deferred NorMuon step as HIP
+        graphs over this plan's tensors, workspace and the second moments Vs."""
+        V = (ctypes.c_void_p * self.n)(*[v.data_ptr() for v in Vs])
+        g = ctypes.c_void_p()
+        _check(lib.dion3_step_normuon_graph_create(self.n, self.groups, self.W, self.M, self.G, self.k,
+                                                   self.idx, V, 1 if has_prev else 0, ctypes.byref(self.params),
+                                                   eta, wd, mu, beta2, nm_eps, _ptr(self.ws), self.ws.numel(),
+                                                   GRAPH_ONE if one else 0, ctypes.byref(g)),
+               "dion3_step_normuon_graph_create")
+        return StepGraph(g, (self, Vs))
 
     def flush_decay(self, mu):
         """Complete the pending decay of the last deferred step on every group."""

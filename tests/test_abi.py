@@ -247,6 +247,9 @@ def test_step_refuses_unsupported_type_pairs():
         assert L.dion3_step_graph_create(2, gr, ptrs, ptrs, ptrs, ks, ptrs, 1, pp, 0.1, 0.0, 0.9, FAKE, sw, 0,
                                          ctypes.byref(out)) == -1
         assert out.value is None
+        assert L.dion3_step_normuon_graph_create(2, gr, ptrs, ptrs, ptrs, ks, ptrs, vs, 1, pp, 0.1, 0.0, 0.9,
+                                                 0.95, 1e-8, FAKE, sw, 0, ctypes.byref(out)) == -1
+        assert out.value is None
     g = d.Group(64, 300, 2, 64 * 300, d.BF16, -1)
     ws = L.dion3_gram_ns_workspace_bytes(ctypes.byref(g), 16, ctypes.byref(b16))
     assert L.dion3_gram_ns(ctypes.byref(g), FAKE, FAKE, 16, ctypes.byref(b16), ctypes.c_void_p(0x2000), FAKE, ws,
@@ -290,6 +293,17 @@ def test_step_graph_argument_checks():
     nulls = (ctypes.c_void_p * 2)(0x1000, None)
     assert L.dion3_step_graph_create(2, groups, nulls, ptrs, ptrs, ks, ptrs, 1, pp, 0.1, 0.0, 0.9, FAKE, sw, 0,
                                      ctypes.byref(out)) == -1
+    assert out.value is None
+    # the NorMuon form: the same checks, and the second-moment pointers
+    vs = (ctypes.c_void_p * 2)(0x3000, 0x4000)
+    nargs = (ptrs, ptrs, ptrs, ks, ptrs)
+    tail = (1, pp, 0.1, 0.0, 0.9, 0.95, 1e-8)
+    NG = L.dion3_step_normuon_graph_create
+    assert NG(2, groups, *nargs, vs, *tail, FAKE, sw - 1, 0, ctypes.byref(out)) == -3
+    assert NG(2, groups, *nargs, vs, *tail, FAKE, sw, 0, None) == -1
+    assert NG(2, groups, *nargs, vs, *tail, FAKE, sw, 2, ctypes.byref(out)) == -1
+    assert NG(2, groups, *nargs, None, *tail, FAKE, sw, 0, ctypes.byref(out)) == -1
+    assert NG(2, groups, *nargs, (ctypes.c_void_p * 2)(0x3000, None), *tail, FAKE, sw, 0, ctypes.byref(out)) == -1
     assert out.value is None
     assert L.dion3_graph_launch(None, None) == -1
     assert L.dion3_graph_destroy(None) == 0

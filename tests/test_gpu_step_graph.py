@@ -2,7 +2,7 @@
 "Dion3: Full-Stack Orthogonal Updates", Section 6: the step's launches have
 the same dependencies every step, so recorded graphs are replayed per step),
 in both forms: per-stream segments replayed on the library's streams, and
-one graph of the whole step.
+one graph of the whole step; the Muon and the NorMuon flavour.
 
 A graph is created once over one set of tensors and replayed several times;
 between replays new gradients are copied in and the same step runs eagerly on
@@ -37,7 +37,7 @@ def _state(shapes, ks, seed0=0):
     return Ws, Ms, Gs, ids
 
 
-def _replays_match(d, shapes, f, replays, seed0=0, one=False):
+def _replays_match(d, shapes, f, replays, seed0=0, one=False, normuon=False):
     ks = [d.dion3_k_from_fraction(min(r, c), f) for r, c, _ in shapes]
     mu, eta = 0.95, 0.02 / math.sqrt(f)
     params = d.make_ns_params(ns_dtype=d.F16)
@@ -45,10 +45,26 @@ def _replays_match(d, shapes, f, replays, seed0=0, one=False):
     B = [[t.clone() for t in ts] for ts in A]
     pa = d.StepPlan(A[0], A[1], A[2], ks, A[3], params)
     pb = d.StepPlan(B[0], B[1], B[2], ks, B[3], params)
-    pa.step_deferred(eta, 0.0, mu, has_prev=False)
-    pb.step_deferred(eta, 0.0, mu, has_prev=False)
+    # NorMuon: second moments per line of the selection axis, one state per copy
+    Va = [torch.zeros(b, min(r, c), dtype=torch.float32, device=DEV) for r, c, b in shapes]
+    Vb = [v.clone() for v in Va]
+
+    def eager(has_prev):
+        if normuon:
+            pa.step_normuon(Va, eta, 0.0, mu, deferred=True, has_prev=has_prev)
+        else:
+            pa.step_deferred(eta, 0.0, mu, has_prev=has_prev)
+
+    eager(False)
+    if normuon:
+        pb.step_normuon(Vb, eta, 0.0, mu, deferred=True, has_prev=False)
+    else:
+        pb.step_deferred(eta, 0.0, mu, has_prev=False)
     torch.cuda.synchronize()
-    graph = pb.graph(eta, 0.0, mu, has_prev=True, one=one)
+    if normuon:
+        graph = pb.graph_normuon(Vb, eta, 0.0, mu, has_prev=True, one=one)
+    else:
+        graph = pb.graph(eta, 0.0, mu, has_prev=True, one=one)
     torch.cuda.synchronize()
     for step in range(1, replays + 1):
         for gi, (r, c, b) in enumerate(shapes):
@@ -57,7 +73,7 @@ def _replays_match(d, shapes, f, replays, seed0=0, one=False):
             B[2][gi].copy_(Gn)
             del Gn
         torch.cuda.synchronize()
-        pa.step_deferred(eta, 0.0, mu, has_prev=True)
+        eager(True)
         torch.cuda.synchronize()
         graph.launch()
         torch.cuda.synchronize()
@@ -65,6 +81,8 @@ def _replays_match(d, shapes, f, replays, seed0=0, one=False):
             assert torch.equal(A[3][gi], B[3][gi]), ("idx", step, gi)
             assert torch.equal(A[0][gi].view(torch.int16), B[0][gi].view(torch.int16)), ("W", step, gi)
             assert torch.equal(A[1][gi].view(torch.int16), B[1][gi].view(torch.int16)), ("M", step, gi)
+            if normuon:
+                assert torch.equal(Va[gi].view(torch.int32), Vb[gi].view(torch.int32)), ("V", step, gi)
     graph.destroy()
     torch.cuda.synchronize()
 
@@ -76,6 +94,14 @@ def test_step_graph_replays_match_eager(d, f, one):
     # at f = 1, and 256 x 256 tiles (the 1024-row groups); the segmented and
     # the single-graph form
     _replays_match(d, [(256, 1024, 6), (1024, 256, 3), (512, 512, 2), (1024, 2048, 2)], f, replays=4, one=one)
+
+
+@pytest.mark.parametrize("one", [False, True])
+def test_normuon_step_graph_replays_match_eager(d, one):
+    """The deferred NorMuon step as graphs (dion3_step_normuon_graph_create):
+    idx, W, M and the second moments V bit-exact after every replay."""
+    _replays_match(d, [(256, 1024, 6), (1024, 256, 3), (512, 512, 2), (1024, 2048, 2)], 0.25, replays=3,
+                   one=one, normuon=True)
 
 
 @pytest.mark.parametrize("one", [False, True])
