@@ -37,7 +37,7 @@ def _state(shapes, ks, seed0=0):
     return Ws, Ms, Gs, ids
 
 
-def _replays_match(d, shapes, f, replays, seed0=0, one=False, normuon=False):
+def _replays_match(d, shapes, f, replays, seed0=0, one=False, normuon=False, wd=0.0):
     ks = [d.dion3_k_from_fraction(min(r, c), f) for r, c, _ in shapes]
     mu, eta = 0.95, 0.02 / math.sqrt(f)
     params = d.make_ns_params(ns_dtype=d.F16)
@@ -51,20 +51,20 @@ def _replays_match(d, shapes, f, replays, seed0=0, one=False, normuon=False):
 
     def eager(has_prev):
         if normuon:
-            pa.step_normuon(Va, eta, 0.0, mu, deferred=True, has_prev=has_prev)
+            pa.step_normuon(Va, eta, wd, mu, deferred=True, has_prev=has_prev)
         else:
-            pa.step_deferred(eta, 0.0, mu, has_prev=has_prev)
+            pa.step_deferred(eta, wd, mu, has_prev=has_prev)
 
     eager(False)
     if normuon:
-        pb.step_normuon(Vb, eta, 0.0, mu, deferred=True, has_prev=False)
+        pb.step_normuon(Vb, eta, wd, mu, deferred=True, has_prev=False)
     else:
-        pb.step_deferred(eta, 0.0, mu, has_prev=False)
+        pb.step_deferred(eta, wd, mu, has_prev=False)
     torch.cuda.synchronize()
     if normuon:
-        graph = pb.graph_normuon(Vb, eta, 0.0, mu, has_prev=True, one=one)
+        graph = pb.graph_normuon(Vb, eta, wd, mu, has_prev=True, one=one)
     else:
-        graph = pb.graph(eta, 0.0, mu, has_prev=True, one=one)
+        graph = pb.graph(eta, wd, mu, has_prev=True, one=one)
     torch.cuda.synchronize()
     for step in range(1, replays + 1):
         for gi, (r, c, b) in enumerate(shapes):
@@ -94,6 +94,14 @@ def test_step_graph_replays_match_eager(d, f, one):
     # at f = 1, and 256 x 256 tiles (the 1024-row groups); the segmented and
     # the single-graph form
     _replays_match(d, [(256, 1024, 6), (1024, 256, 3), (512, 512, 2), (1024, 2048, 2)], f, replays=4, one=one)
+
+
+@pytest.mark.parametrize("normuon", [False, True])
+def test_step_graph_with_weight_decay(d, normuon):
+    """Weight decay on: the graph also holds the decay of the lines the update
+    does not touch (a kernel of its own after a fused update)."""
+    _replays_match(d, [(256, 1024, 4), (1024, 256, 2), (1024, 2048, 2)], 0.25, replays=3, normuon=normuon,
+                   wd=0.01)
 
 
 @pytest.mark.parametrize("one", [False, True])
