@@ -119,6 +119,13 @@ def test_step_graph_7b_matches_eager(d, one):
     _replays_match(d, synth.shape_groups("7b"), 0.25, replays=2, seed0=0, one=one)
 
 
+@pytest.mark.timeout(600)
+def test_normuon_step_graph_7b_matches_eager(d):
+    """The NorMuon flavour of the benchmarked workload as segmented graphs:
+    7B shape set, f = 1/4, two replays, V bit-exact as well."""
+    _replays_match(d, synth.shape_groups("7b"), 0.25, replays=2, seed0=0, normuon=True)
+
+
 def test_step_graph_after_release(d):
     """dion3_release destroys the library's streams: a segmented graph built
     on them then refuses to launch (DION3_ERR_INVALID_ARG, nothing enqueued),
