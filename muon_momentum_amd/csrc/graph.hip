@@ -253,10 +253,10 @@ extern "C" int dion3_step_normuon_graph_create(int n_groups, const dion3_group* 
   if (!out) return DION3_ERR_INVALID_ARG;
   *out = nullptr;
   if (flags & ~(unsigned)DION3_GRAPH_ONE) return DION3_ERR_INVALID_ARG;
-  if (!V) return DION3_ERR_INVALID_ARG;
-  for (int i = 0; i < n_groups && V; ++i)
-    if (!V[i]) return DION3_ERR_INVALID_ARG;
   if (int st = check_step_args(n_groups, groups, W, M, G, k, idx, p, ws, ws_bytes)) return st;
+  if (!V) return DION3_ERR_INVALID_ARG;
+  for (int i = 0; i < n_groups; ++i)
+    if (!V[i]) return DION3_ERR_INVALID_ARG;
   return build_step_graph(flags, out, [&] {
     return dion3_step_normuon(n_groups, groups, W, M, G, k, idx, V, 1, has_prev, p, eta, wd, mu, beta2, nm_eps,
                               ws, ws_bytes, nullptr);
